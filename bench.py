@@ -1,0 +1,229 @@
+"""Benchmark of the DeepSeek-V4.1 low-ratio compressed-KV hot path on one
+MI355X.
+
+One step = one pass of both halves of the path over one batch:
+  1. compress-store: ratio-2 ragged prefill of 16 requests totalling 32,768
+     tokens (fused |kv|score| bf16 [32768, 1024], page 128, V41_FP4 cache);
+  2. dequant-gather: 262,144 distinct ids from a V41 cache of 1,048,576 rows
+     (16,384 pages x 64, random page table) into bf16 [262144, 512].
+Inputs are seeded synthetic data, resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is compressed KV rows per second over the
+step (rows compressed + rows gathered); the per-kernel HBM rates, the roofline
+object of the dominant kernel (the gather) and the CPU-oracle baseline ride
+along.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["fp8_fp4_quantized_amd/csrc/store_gather.hip",
+                  "fp8_fp4_quantized_amd/csrc/row_ops.hpp",
+                  "fp8_fp4_quantized_amd/csrc/codec.hpp",
+                  "fp8_fp4_quantized_amd/csrc/layout.hpp",
+                  "fp8_fp4_quantized_amd/csrc/wave.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or
+    None when the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gather-blocks", type=int, default=0)
+    ap.add_argument("--compress-blocks", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path runs on one GPU's share); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fp8_fp4_quantized_amd as kvc
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kvc.kvc_set_launch_shape(args.gather_blocks, args.compress_blocks)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.time()
+    c3 = W.workload_c3()
+    c4 = W.workload_c4()
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+    lengths = c3["lengths"].astype(np.int64)
+    c3_rows = int((lengths // 2).sum())              # P = 0: one row per complete pair
+    c3_tails = int((lengths % 2).sum())
+    fp4 = kvc.kvc_layout_query("V41_FP4")
+    v41 = kvc.kvc_layout_query("V41")
+
+    proj = d(c3["kv"])
+    c3_args = dict(
+        ratio=2, mode=kvc.MODE_PREFILL, kv=proj[:, :512], score=proj[:, 512:],
+        start_pos=d(c3["start_pos"]), offsets=d(c3["offsets"]), page_table=d(c3["page_table"]),
+        state=d(c3["state"]), norm_w=d(c3["norm_w"]), eps=c3["eps"], freqs=d(c3["freqs"]),
+        latent_out=torch.empty((c3_rows, 512), dtype=torch.int16, device=dev),
+        cache=kvc.Cache(torch.zeros((c3["num_pages"], 128 * fp4.row_bytes), dtype=torch.uint8,
+                                    device=dev), "V41_FP4", 128))
+    g_cache = kvc.Cache(d(c4["cache"]), "V41", 64)
+    g_pt, g_ids = d(c4["page_table"]), d(c4["ids"])
+    n_ids = int(c4["ids"].size)
+    g_out = torch.empty((n_ids, 512), dtype=torch.int16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        kvc.kvc_compress_store(**c3_args, status=status)
+        if ev is not None:
+            ev[1].record(stream)
+        kvc.kvc_dequant_gather(g_cache, g_pt, g_ids, g_out, status)
+        if ev is not None:
+            ev[2].record(stream)
+
+    # ---------------------------------------------------------------- timing
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, f"device status {int(status.item())}"
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    comp_ms = [e[0].elapsed_time(e[1]) for e in events]
+    gath_ms = [e[1].elapsed_time(e[2]) for e in events]
+    ms_step = elapsed * 1e3 / args.steps
+
+    comp_bytes = c3_rows * (4096 + 1024 + fp4.row_bytes) + c3_tails * 2 * 2048
+    gath_bytes = n_ids * (v41.row_bytes + 1024 + 4)
+    comp_s = float(np.mean(comp_ms)) / 1e3
+    gath_s = float(np.mean(gath_ms)) / 1e3
+    comp_gbs = comp_bytes / comp_s / 1e9
+    gath_gbs = gath_bytes / gath_s / 1e9
+    rows_step = c3_rows + n_ids
+    value = rows_step / (ms_step / 1e3)
+    log(f"compress: {np.mean(comp_ms)*1e3:.1f} us  {comp_gbs:.0f} GB/s  "
+        f"gather: {np.mean(gath_ms)*1e3:.1f} us  {gath_gbs:.0f} GB/s  step {ms_step*1e3:.1f} us")
+
+    traffic = measured_traffic("dequant_gather")
+    out = {
+        "metric": "compressed KV rows/sec + achieved HBM GB/s (compress-store, dequant-gather)",
+        "value": value,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill compress-store (ratio 2, 16 requests, 32768 tokens, fused "
+                        "|kv|score| bf16 [32768,1024], page 128, V41_FP4) + sparse-prefill "
+                        "dequant-gather (262144 ids from a 1048576-row V41 cache, page 64, "
+                        "random page table -> bf16 [262144,512])",
+            "compress_rows": c3_rows, "gather_rows": n_ids,
+            "seed_c3": int(c3["seed"]), "odd_lengths": c3_tails,
+        },
+        "hbm_gbps": (comp_bytes + gath_bytes) / (ms_step / 1e3) / 1e9,
+        "kernels": {
+            "compress_store": {"us": float(np.mean(comp_ms)) * 1e3, "p90_us": float(np.percentile(comp_ms, 90)) * 1e3,
+                               "bytes": comp_bytes, "gbps": comp_gbs, "frac": comp_gbs / HBM_PEAK_GBS,
+                               "rows_per_s": c3_rows / comp_s},
+            "dequant_gather": {"us": float(np.mean(gath_ms)) * 1e3, "p90_us": float(np.percentile(gath_ms, 90)) * 1e3,
+                               "bytes": gath_bytes, "gbps": gath_gbs, "frac": gath_gbs / HBM_PEAK_GBS,
+                               "rows_per_s": n_ids / gath_s},
+        },
+        "roofline": {"bound": "hbm", "achieved": gath_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gath_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "dequant_gather", "algorithmic_bytes": gath_bytes},
+        "cpu_baseline": None,
+    }
+
+    # ---------------------------------------------------------------- oracle
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.num_threads()
+        # bounded sample: the first 4 requests of the compress batch and the
+        # first 65,536 gather ids, repeated until ~10 s of CPU work
+        n4 = int(lengths[:4].sum())
+        sub = dict(c3)
+        sub_off = c3["offsets"][:, :4].copy()
+        rows_sub = int((lengths[:4] // 2).sum())
+        m = 65536
+        ids_sub = c4["ids"][:m]
+        reps, spent, done_rows = 0, 0.0, 0
+        while spent < 10.0 and reps < 20:
+            cache_h = np.zeros((c3["num_pages"], 128 * fp4.row_bytes), np.uint8)
+            t = time.perf_counter()
+            oracle.compress(ratio=2, mode=oracle.PREFILL, kv=c3["kv"][:n4], fused=True,
+                            offsets=sub_off, start_pos=c3["start_pos"][:4],
+                            page_table=c3["page_table"][:4], state=c3["state"][:4].copy(),
+                            norm_w=c3["norm_w"], eps=c3["eps"], freqs=c3["freqs"], cache=cache_h,
+                            layout="V41_FP4", page_size=128, want_prequant=False)
+            oracle.dequant_gather(c4["cache"], "V41", 64, c4["page_table"], ids_sub)
+            spent += time.perf_counter() - t
+            done_rows += rows_sub + m
+            reps += 1
+        out["cpu_baseline"] = {"value": done_rows / spent, "unit": "rows/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"{reps} x (compress of the first 4 requests = "
+                                         f"{rows_sub} rows + gather of the first {m} ids), "
+                                         f"{spent:.1f} s"}
+        del sub
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

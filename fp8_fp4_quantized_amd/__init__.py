@@ -1,0 +1,231 @@
+"""Python binding of ``libkvc.so``: the MI355X (gfx950) compressed-KV store
+and gather for DeepSeek-V4.1 low-ratio layers (C ABI in ``include/kvc.h``).
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of
+``libkvc.so``; PyTorch provides device memory and the current stream.  There
+is no fallback: importing this package without the built library raises.
+
+Function names are those of the C ABI.  Tensors are CUDA (HIP) tensors:
+bf16 rows may be ``torch.bfloat16`` or ``int16``/``uint16`` bit patterns;
+caches are ``uint8`` tensors ``[num_pages, page_stride]``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch  # noqa: F401  (loads the HIP runtime that libkvc.so then binds to)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvc.so")
+
+KVC_OK, KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ELAUNCH = 0, -1, -2, -3
+LAYOUT_V4, LAYOUT_V41, LAYOUT_V41_FP4 = 0, 1, 2
+LAYOUTS = {"V4": LAYOUT_V4, "V41": LAYOUT_V41, "V41_FP4": LAYOUT_V41_FP4}
+MODE_PREFILL, MODE_DECODE = 0, 1
+STATUS_ID_RANGE, STATUS_PAGE_RANGE, STATUS_PT_RANGE = 1, 2, 4
+STATUS_LATENT_RANGE, STATUS_POS_RANGE = 8, 16
+
+
+class KvcError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"kvc error {code}: {msg}")
+        self.code = code
+
+
+class kvc_layout_info(C.Structure):
+    _fields_ = [("data_bytes", C.c_int32), ("scale_bytes", C.c_int32),
+                ("row_bytes", C.c_int32), ("group", C.c_int32), ("quant_dims", C.c_int32)]
+
+
+class kvc_cache(C.Structure):
+    _fields_ = [("base", C.c_void_p), ("layout", C.c_int32), ("page_size", C.c_int32),
+                ("page_stride", C.c_int64), ("num_pages", C.c_int64)]
+
+
+class kvc_compress_args(C.Structure):
+    _fields_ = [
+        ("ratio", C.c_int32), ("mode", C.c_int32),
+        ("kv", C.c_void_p), ("kv_stride", C.c_int64),
+        ("score", C.c_void_p), ("score_stride", C.c_int64),
+        ("num_slots", C.c_int32),
+        ("offsets", C.c_void_p), ("start_pos", C.c_void_p),
+        ("page_table", C.c_void_p), ("pt_stride", C.c_int64),
+        ("out_loc", C.c_void_p), ("state", C.c_void_p),
+        ("norm_w", C.c_void_p), ("eps", C.c_float),
+        ("freqs", C.c_void_p), ("max_pos", C.c_int64),
+        ("latent_out", C.c_void_p), ("latent_stride", C.c_int64), ("max_out_rows", C.c_int64),
+        ("prequant_out", C.c_void_p), ("prequant_stride", C.c_int64),
+        ("cache", kvc_cache), ("status", C.c_void_p),
+    ]
+
+
+# symbol -> (restype, argtypes); the same list as include/kvc.h
+_VP, _I32, _I64 = C.c_void_p, C.c_int32, C.c_int64
+SIGNATURES = {
+    "kvc_layout_query": (C.c_int, [_I32, C.POINTER(kvc_layout_info)]),
+    "kvc_store_rows": (C.c_int, [C.POINTER(kvc_cache), _VP, _I64, _VP, _I64, _VP, _VP]),
+    "kvc_compress_store": (C.c_int, [C.POINTER(kvc_compress_args), _VP]),
+    "kvc_dequant_gather": (C.c_int, [C.POINTER(kvc_cache), _VP, _I64, _VP, _I64, _VP, _I64, _VP, _VP]),
+    "kvc_kvbuf_create": (_VP, []),
+    "kvc_kvbuf_destroy": (None, [_VP]),
+    "kvc_kvbuf_forget": (None, [_VP]),
+    "kvc_kvbuf_begin_forward": (None, [_VP]),
+    "kvc_dequant_gather_reuse": (C.c_int, [_VP, C.POINTER(kvc_cache), _VP, _I64, _VP, _I64, _VP,
+                                           _I64, _VP, _VP, _VP]),
+    "kvc_last_error": (C.c_char_p, []),
+    "kvc_version": (C.c_int, []),
+    "kvc_set_launch_shape": (C.c_int, [_I32, _I32]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded ``libkvc.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m fp8_fp4_quantized_amd.build` or __graft_entry__.build()")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+lib()   # fail loudly at import when the HIP library is missing
+
+
+def _check(rc: int) -> None:
+    if rc != KVC_OK:
+        raise KvcError(rc, lib().kvc_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+@dataclass
+class Cache:
+    """A paged cache: ``data`` is a uint8 tensor ``[num_pages, page_stride]``."""
+    data: torch.Tensor
+    layout: int
+    page_size: int
+
+    def desc(self) -> kvc_cache:
+        assert self.data.dtype == torch.uint8 and self.data.dim() == 2 and self.data.is_contiguous()
+        lay = LAYOUTS[self.layout] if isinstance(self.layout, str) else int(self.layout)
+        return kvc_cache(self.data.data_ptr(), lay, self.page_size,
+                         self.data.shape[1], self.data.shape[0])
+
+
+# --------------------------------------------------------------------- calls
+def kvc_version() -> int:
+    return lib().kvc_version()
+
+
+def kvc_last_error() -> str:
+    return lib().kvc_last_error().decode()
+
+
+def kvc_layout_query(layout) -> kvc_layout_info:
+    info = kvc_layout_info()
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    _check(lib().kvc_layout_query(lay, C.byref(info)))
+    return info
+
+
+def kvc_set_launch_shape(gather_blocks: int = 0, compress_blocks: int = 0) -> None:
+    _check(lib().kvc_set_launch_shape(gather_blocks, compress_blocks))
+
+
+def kvc_store_rows(cache: Cache, rows: torch.Tensor, out_loc: torch.Tensor,
+                   status: torch.Tensor | None = None, stream=None) -> None:
+    """Quantize bf16 ``rows [n, >=512]`` into ``cache`` at ``out_loc [n]``."""
+    d = cache.desc()
+    _check(lib().kvc_store_rows(C.byref(d), rows.data_ptr(), rows.stride(0), out_loc.data_ptr(),
+                                rows.shape[0], _ptr(status), _stream(stream)))
+
+
+def kvc_dequant_gather(cache: Cache, page_table: torch.Tensor | None, ids: torch.Tensor,
+                       out: torch.Tensor, status: torch.Tensor | None = None, stream=None) -> None:
+    """``out[j] = bf16 row of ids[j]`` (through ``page_table`` when given)."""
+    d = cache.desc()
+    n_pages = 0 if page_table is None else page_table.numel()
+    _check(lib().kvc_dequant_gather(C.byref(d), _ptr(page_table), n_pages, ids.data_ptr(),
+                                    ids.numel(), out.data_ptr(), out.stride(0), _ptr(status),
+                                    _stream(stream)))
+
+
+class KVBuf:
+    """Dequant-reuse head (``kvc_kvbuf``): a gather whose arguments match the
+    last one it ran is skipped."""
+
+    def __init__(self):
+        self._h = lib().kvc_kvbuf_create()
+        if not self._h:
+            raise MemoryError("kvc_kvbuf_create")
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _lib is not None:
+            _lib.kvc_kvbuf_destroy(h)
+
+    def forget(self) -> None:
+        lib().kvc_kvbuf_forget(self._h)
+
+    def begin_forward(self) -> None:
+        lib().kvc_kvbuf_begin_forward(self._h)
+
+    def kvc_dequant_gather_reuse(self, cache: Cache, page_table, ids, out, status=None,
+                                 stream=None) -> bool:
+        d = cache.desc()
+        hit = C.c_int32(0)
+        n_pages = 0 if page_table is None else page_table.numel()
+        _check(lib().kvc_dequant_gather_reuse(self._h, C.byref(d), _ptr(page_table), n_pages,
+                                              ids.data_ptr(), ids.numel(), out.data_ptr(),
+                                              out.stride(0), _ptr(status), C.byref(hit),
+                                              _stream(stream)))
+        return bool(hit.value)
+
+
+def kvc_compress_store(*, ratio: int, mode: int, kv: torch.Tensor, score: torch.Tensor | None,
+                       start_pos: torch.Tensor, cache: Cache, norm_w: torch.Tensor, eps: float,
+                       freqs: torch.Tensor, latent_out: torch.Tensor, max_out_rows: int | None = None,
+                       offsets: torch.Tensor | None = None, page_table: torch.Tensor | None = None,
+                       out_loc: torch.Tensor | None = None, state: torch.Tensor | None = None,
+                       prequant_out: torch.Tensor | None = None, status: torch.Tensor | None = None,
+                       stream=None) -> None:
+    """The fused compressor.  ``kv``/``score`` are 2-D views whose row stride
+    is passed through (a fused ``|kv|score|`` buffer ``proj [T, 1024]`` is
+    ``kv=proj[:, :512], score=proj[:, 512:]``)."""
+    a = kvc_compress_args()
+    a.ratio, a.mode = ratio, mode
+    a.kv, a.kv_stride = kv.data_ptr(), kv.stride(0)
+    a.score = _ptr(score)
+    a.score_stride = 0 if score is None else score.stride(0)
+    a.num_slots = start_pos.numel()
+    a.offsets, a.start_pos = _ptr(offsets), start_pos.data_ptr()
+    a.page_table = _ptr(page_table)
+    a.pt_stride = 0 if page_table is None else page_table.shape[-1]
+    a.out_loc, a.state = _ptr(out_loc), _ptr(state)
+    a.norm_w, a.eps = norm_w.data_ptr(), eps
+    a.freqs, a.max_pos = freqs.data_ptr(), freqs.shape[0]
+    a.latent_out, a.latent_stride = latent_out.data_ptr(), latent_out.stride(0)
+    a.max_out_rows = latent_out.shape[0] if max_out_rows is None else max_out_rows
+    a.prequant_out = _ptr(prequant_out)
+    a.prequant_stride = 0 if prequant_out is None else prequant_out.stride(0)
+    a.cache = cache.desc()
+    a.status = _ptr(status)
+    _check(lib().kvc_compress_store(C.byref(a), _stream(stream)))

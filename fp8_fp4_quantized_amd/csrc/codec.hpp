@@ -1,0 +1,107 @@
+// codec.hpp -- bit-exact number-format conversions for the KV row codecs.
+//
+// Formats: bfloat16; OCP fp8 e4m3fn (bias 7, max 448, 0x7F/0xFF NaN);
+// OCP fp4 e2m1 (values 0, .5, 1, 1.5, 2, 3, 4, 6); ue8m0 (a bare biased
+// exponent).  Encoders round to nearest, ties to even, and work on integer
+// bit fields so the result does not depend on any hardware rounding mode.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even
+// (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// |x| ordering of finite bf16 values equals the integer ordering of their
+// low 15 bits, so a group's amax is an integer max
+__device__ __forceinline__ uint32_t absmax_bf16x8(uint4 x) {
+  const uint32_t m = 0x7FFF7FFFu;
+  uint32_t a = max(x.x & m, x.y & m), b = max(x.z & m, x.w & m);
+  uint32_t c = max(a, b);                  // two lane-wise maxima, lo and hi halves
+  return max(c & 0xFFFFu, c >> 16);
+}
+
+// ue8m0 scale exponent of a group from the fp32 bits of its amax: the
+// closed form of 127 + ceil(log2(max(amax / 448, 1e-4))) given in sglang PR
+// #39652, Review.  amax / 448 = 2^(e - 135) (1 + f) / 1.75, whose log2 rounds
+// up past e - 135 exactly when the mantissa exceeds 0.75 (0x600000); the
+// floor of 114 is the 1e-4 clamp (ceil(log2 1e-4) = -13).
+__device__ __forceinline__ int ue8m0_from_amax_bits(uint32_t b) {
+  const int e = (int)(b >> 23) - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e > 114 ? e : 114;
+}
+
+// fp8 e4m3fn code of the bf16 value h scaled by 2^(127 - E).  The caller
+// guarantees |h| * 2^(127-E) <= 448 and E >= 114 (the ue8m0 exponent of h's
+// group), so there is no overflow and bf16 subnormals round to zero.
+__device__ __forceinline__ uint32_t fp8_from_bf16(uint32_t h, int E) {
+  const uint32_t sign = (h >> 8) & 0x80u;
+  const int bexp = (int)((h >> 7) & 0xFFu);
+  const uint32_t mant = h & 0x7Fu;
+  const int fe = bexp - E + 7;             // e4m3 biased exponent when normal
+  // normal: keep 3 of the 7 mantissa bits, nearest even; a carry bumps fe
+  const uint32_t rn = (mant + 7u + ((mant >> 4) & 1u)) >> 4;
+  const uint32_t normal = ((uint32_t)fe << 3) + rn;
+  // subnormal (fe <= 0): (128 + mant) * 2^(fe - 5) units of 2^-9, nearest
+  // even; shifts past 9 leave less than half a unit, as 9 does
+  int sh = 5 - fe;
+  sh = sh > 9 ? 9 : (sh < 1 ? 1 : sh);
+  const uint32_t v = 128u + mant;
+  const uint32_t q = v >> sh;
+  const uint32_t rem = v & ((1u << sh) - 1u);
+  const uint32_t half = 1u << (sh - 1);
+  const uint32_t sub = q + ((rem > half) || (rem == half && (q & 1u)) ? 1u : 0u);
+  uint32_t code = fe >= 1 ? normal : sub;
+  code = bexp == 0 ? 0u : code;
+  return code | sign;
+}
+
+// e4m3fn code of a non-negative finite fp32, nearest even, clamped at 448
+// (0x7E).  Used for the FP4 group scale.
+__device__ __forceinline__ uint32_t e4m3_satfinite(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const int fe = (int)(u >> 23) - 120;
+  const uint32_t m = u & 0x7FFFFFu;
+  const uint32_t rn = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;
+  uint32_t normal = ((uint32_t)fe << 3) + rn;
+  normal = fe >= 16 ? 0x7Eu : (normal > 0x7Eu ? 0x7Eu : normal);
+  const uint32_t sub = (uint32_t)__builtin_rintf(f * 512.0f);   // below 2^-6: k * 2^-9
+  return fe >= 1 ? normal : sub;
+}
+
+// exact fp32 value of an e4m3fn code (NaN codes excluded by the caller)
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const float sub = (float)m * 0x1p-9f;
+  const float mag = e == 0 ? sub : nrm;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// e2m1 code of the bf16 value h for the scale s > 0: the nearest grid value
+// of |h| / s, decided by exact comparisons of |h| with the midpoints times s
+// (each product has at most 7 significant bits, so it is exact in fp32);
+// equality at a midpoint goes to the even code.
+struct Fp4Thresholds {
+  float t0, t1, t2, t3, t4, t5, t6;
+};
+__device__ __forceinline__ Fp4Thresholds fp4_thresholds(float s) {
+  return {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
+}
+__device__ __forceinline__ uint32_t fp4_from_bf16(uint32_t h, const Fp4Thresholds& t) {
+  const float a = __uint_as_float((h & 0x7FFFu) << 16);
+  const uint32_t c = (a > t.t0) + (a >= t.t1) + (a > t.t2) + (a >= t.t3) + (a > t.t4) +
+                     (a >= t.t5) + (a > t.t6);
+  return c | ((h >> 12) & 0x8u);
+}
+
+}  // namespace kvc

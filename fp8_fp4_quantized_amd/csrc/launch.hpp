@@ -1,0 +1,81 @@
+// launch.hpp -- parameter blocks and launchers shared by the C ABI and the
+// kernel translation units (host-side declarations only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+struct CacheView {
+  uint8_t* base;
+  int64_t page_stride;
+  int64_t num_pages;
+  int32_t page_bits;
+  int32_t layout;
+};
+
+struct StoreParams {
+  CacheView cache;
+  const uint16_t* rows;
+  int64_t row_stride;          // elements
+  const int32_t* out_loc;
+  int64_t n;
+  int32_t* status;
+};
+
+struct GatherParams {
+  CacheView cache;
+  const int32_t* page_table;   // nullable
+  int64_t n_pages;
+  const int32_t* ids;
+  int64_t n;
+  uint16_t* out;
+  int64_t out_stride;          // elements
+  int32_t* status;
+};
+
+struct CompressParams {
+  CacheView cache;
+  int32_t ratio;
+  int32_t mode;                // 0 prefill, 1 decode
+  const uint16_t* kv;
+  int64_t kv_stride;
+  const uint16_t* score;
+  int64_t score_stride;
+  int32_t num_slots;
+  const int32_t* offsets;
+  const int32_t* start_pos;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const int32_t* out_loc;
+  uint16_t* state;
+  const uint16_t* norm_w;
+  float eps;
+  const float* freqs;
+  int64_t max_pos;
+  uint16_t* latent;
+  int64_t latent_stride;
+  int64_t max_out_rows;
+  uint16_t* prequant;
+  int64_t prequant_stride;
+  int32_t* status;
+};
+
+// Each launcher enqueues one kernel on `stream` and returns the HIP error of
+// the launch (hipSuccess on success).
+hipError_t launch_store_rows(const StoreParams& p, hipStream_t stream);
+hipError_t launch_dequant_gather(const GatherParams& p, hipStream_t stream);
+hipError_t launch_compress(const CompressParams& p, hipStream_t stream);
+
+// largest num_slots a prefill compress accepts (its LDS tables)
+int max_prefill_slots();
+
+// launch-shape overrides for tuning sweeps (0 = default)
+struct LaunchTuning {
+  int gather_blocks;           // workgroups of the gather grid
+  int compress_blocks;         // workgroups of the prefill compress grid
+};
+LaunchTuning& launch_tuning();
+
+}  // namespace kvc

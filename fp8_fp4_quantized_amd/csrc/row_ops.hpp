@@ -1,0 +1,205 @@
+// row_ops.hpp -- one row of 512 dims on one wavefront: quantize-and-store
+// (the single row quantizer of sglang PR #39652, Summary) and the per-lane
+// dequantizer of the gather.
+//
+// Lane l owns dims [8l, 8l + 8) as a uint4 of four packed bf16 pairs (the even
+// dim in the low half).  Group maxima are DPP reductions over the 4 (V41),
+// 2 (V41_FP4) or 8 (V4) lanes of a scale group.
+#pragma once
+
+#include "codec.hpp"
+#include "layout.hpp"
+#include "wave.hpp"
+
+namespace kvc {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_u4(const void* p) {
+  const u32x4 v = *(const u32x4*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld_u4_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_u4(void* p, uint4 v) {
+  *(u32x4*)p = u32x4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ void st_u4_nt(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4*)p);
+}
+
+// byte k of a word
+__device__ __forceinline__ uint32_t byte_of(uint32_t w, int k) { return (w >> (8 * k)) & 0xFFu; }
+
+// Gather the scale byte held by lane `stride * g` (g = 0 .. 4*W-1) into W
+// dwords, byte g of the result in byte g % 4 of dword g / 4.  Uses
+// v_readlane, so the result is wave-uniform.
+template <int W, int Stride>
+__device__ __forceinline__ void collect_scale_bytes(uint32_t v, uint32_t (&out)[W]) {
+#pragma unroll
+  for (int d = 0; d < W; ++d) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, (4 * d + k) * Stride);
+      w |= (b & 0xFFu) << (8 * k);
+    }
+    out[d] = w;
+  }
+}
+
+// ------------------------------------------------------------------ store_row
+// Quantize the row held by the wave (x = this lane's 8 dims) and write it to
+// `data` / `scale` (the row's parts in its page).  Every lane of the wave
+// must call this (the group reductions read neighbouring lanes); `write` is
+// wave-uniform.
+template <int L>
+__device__ __forceinline__ void store_row_wave(uint4 x, uint8_t* data, uint8_t* scale, bool write);
+
+template <>
+__device__ __forceinline__ void store_row_wave<kV41>(uint4 x, uint8_t* data, uint8_t* scale,
+                                                     bool write) {
+  const int lane = lane_id();
+  const uint32_t amax = group_max_u32<4>(absmax_bf16x8(x));     // 32 dims = 4 lanes
+  const int E = ue8m0_from_amax_bits(amax << 16);
+  const uint32_t h[8] = {x.x & 0xFFFFu, x.x >> 16, x.y & 0xFFFFu, x.y >> 16,
+                         x.z & 0xFFFFu, x.z >> 16, x.w & 0xFFFFu, x.w >> 16};
+  uint32_t c[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) c[k] = fp8_from_bf16(h[k], E);
+  const uint32_t w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  const uint32_t w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  uint32_t sc[4];
+  collect_scale_bytes<4, 4>((uint32_t)E, sc);
+  if (!write) return;
+  *(u32x2*)(data + 8 * lane) = u32x2{w0, w1};
+  if (lane == 0) st_u4(scale, make_uint4(sc[0], sc[1], sc[2], sc[3]));
+}
+
+template <>
+__device__ __forceinline__ void store_row_wave<kV4>(uint4 x, uint8_t* data, uint8_t* scale,
+                                                    bool write) {
+  const int lane = lane_id();
+  const uint32_t amax = group_max_u32<8>(absmax_bf16x8(x));     // 64 dims = 8 lanes
+  const int E = ue8m0_from_amax_bits(amax << 16);
+  const uint32_t h[8] = {x.x & 0xFFFFu, x.x >> 16, x.y & 0xFFFFu, x.y >> 16,
+                         x.z & 0xFFFFu, x.z >> 16, x.w & 0xFFFFu, x.w >> 16};
+  uint32_t c[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) c[k] = fp8_from_bf16(h[k], E);
+  const uint32_t w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  const uint32_t w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  uint32_t sc[2];
+  collect_scale_bytes<2, 8>((uint32_t)E, sc);     // lanes 0, 8, .., 56; the 8th is rope
+  sc[1] &= 0x00FFFFFFu;                            // pad byte = 0
+  if (!write) return;
+  if (lane < kRopeLane0) {
+    *(u32x2*)(data + 8 * lane) = u32x2{w0, w1};
+  } else {                                         // rope dims kept as bf16
+    st_u4(data + kNope + 16 * (lane - kRopeLane0), x);
+  }
+  if (lane == 0) *(u32x2*)scale = u32x2{sc[0], sc[1]};
+}
+
+template <>
+__device__ __forceinline__ void store_row_wave<kV41Fp4>(uint4 x, uint8_t* data, uint8_t* scale,
+                                                        bool write) {
+  const int lane = lane_id();
+  const uint32_t amax = group_max_u32<2>(absmax_bf16x8(x));     // 16 dims = 2 lanes
+  // scale = e4m3(amax / 6), fp32 division correctly rounded
+  const float q = __fdiv_rn(__uint_as_float(amax << 16), 6.0f);
+  const uint32_t sc = e4m3_satfinite(q);
+  const float s = e4m3_to_f32(sc);
+  const Fp4Thresholds t = fp4_thresholds(s);
+  const uint32_t h[8] = {x.x & 0xFFFFu, x.x >> 16, x.y & 0xFFFFu, x.y >> 16,
+                         x.z & 0xFFFFu, x.z >> 16, x.w & 0xFFFFu, x.w >> 16};
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w |= fp4_from_bf16(h[k], t) << (4 * k);
+  w = sc == 0 ? 0u : w;                            // zero scale: all codes 0
+  uint32_t sb[8];
+  collect_scale_bytes<8, 2>(sc, sb);
+  if (!write) return;
+  *(uint32_t*)(data + 4 * lane) = w;
+  if (lane == 0) {
+    st_u4(scale, make_uint4(sb[0], sb[1], sb[2], sb[3]));
+    st_u4(scale + 16, make_uint4(sb[4], sb[5], sb[6], sb[7]));
+  }
+}
+
+// ------------------------------------------------------------------ dequant
+// fp8 e4m3fn codes (4 per word) times 2^(E - 127) -> 4 bf16 (two words).
+// Fast path: for 3 <= E <= 254 the product is exact in bf16 or overflows to
+// infinity in fp32, so the top half of the fp32 product is the answer.  The
+// fp32 built from the code's low 7 bits placed at bit 20 equals the code's
+// value times 2^-120 for normal and subnormal codes alike (fp32 denormals
+// are kept on gfx950), and ldexp adds E - 7.
+__device__ __forceinline__ float fp8_scaled(uint32_t c, int E) {
+  const float f = __uint_as_float(((c & 0x80u) << 24) | ((c & 0x7Fu) << 20));
+  return __builtin_amdgcn_ldexpf(f, E - 7);
+}
+__device__ __forceinline__ uint32_t bf16_top(float f) { return __float_as_uint(f) >> 16; }
+
+__device__ __forceinline__ uint2 dq_fp8x4_fast(uint32_t w, int E) {
+  const uint32_t b0 = bf16_top(fp8_scaled(w & 0xFFu, E));
+  const uint32_t b1 = bf16_top(fp8_scaled((w >> 8) & 0xFFu, E));
+  const uint32_t b2 = bf16_top(fp8_scaled((w >> 16) & 0xFFu, E));
+  const uint32_t b3 = bf16_top(fp8_scaled(w >> 24, E));
+  return make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+}
+
+// general path: any E (255 = NaN scale), NaN codes, and rounding of the
+// products that fall below the bf16 subnormal grid (E <= 2)
+__device__ __forceinline__ uint32_t dq_fp8_general(uint32_t c, int E) {
+  if (E == 255 || (c & 0x7Fu) == 0x7Fu) return 0x7FC0u;
+  uint32_t u = __float_as_uint(fp8_scaled(c, E));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint2 dq_fp8x4_general(uint32_t w, int E) {
+  return make_uint2(dq_fp8_general(w & 0xFFu, E) | (dq_fp8_general((w >> 8) & 0xFFu, E) << 16),
+                    dq_fp8_general((w >> 16) & 0xFFu, E) | (dq_fp8_general(w >> 24, E) << 16));
+}
+
+// any byte of w equal to 0x7F or 0xFF (an e4m3fn NaN)
+__device__ __forceinline__ bool has_nan_fp8(uint32_t w) {
+  return (((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) != 0u;
+}
+
+// 8 fp8 codes + their ue8m0 exponent -> 8 bf16
+__device__ __forceinline__ uint4 dq_fp8x8(uint2 codes, int E) {
+  uint2 lo, hi;
+  if ((unsigned)(E - 3) <= 251u && !has_nan_fp8(codes.x) && !has_nan_fp8(codes.y)) {
+    lo = dq_fp8x4_fast(codes.x, E);
+    hi = dq_fp8x4_fast(codes.y, E);
+  } else {
+    lo = dq_fp8x4_general(codes.x, E);
+    hi = dq_fp8x4_general(codes.y, E);
+  }
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// 8 e2m1 codes (nibbles, dim order from the low nibble) + their e4m3 scale
+// code -> 8 bf16.  The e2m1 magnitude's low 3 bits placed at bit 22 of an
+// fp32 give the value times 2^-126; the product with the scale is exact
+// (at most 7 significant bits, far from the fp32 and bf16 limits).
+__device__ __forceinline__ uint32_t dq_fp4_one(uint32_t n, float s) {
+  const float f = __uint_as_float(((n & 0x8u) << 28) | ((n & 0x7u) << 22));
+  return bf16_top(__builtin_amdgcn_ldexpf(f * s, 126));
+}
+__device__ __forceinline__ uint4 dq_fp4x8(uint32_t w, uint32_t sc) {
+  if ((sc & 0x7Fu) == 0x7Fu) return make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+  const float s = e4m3_to_f32(sc);
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t b = w >> (8 * k);
+    o[k] = dq_fp4_one(b & 0xFu, s) | (dq_fp4_one((b >> 4) & 0xFu, s) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+}  // namespace kvc

@@ -1,0 +1,199 @@
+// store_gather.hip -- plain quantize-store of bf16 rows and the paged
+// dequant-gather (gfx950).
+//
+// Both kernels put one 512-dim row on one 64-lane wave (8 dims per lane), so
+// every global access of a row is one contiguous, fully used span: the bf16
+// row (1024 B), the data part (512 / 256 / 576 B) and the scale part.  A wave
+// runs several rows per loop trip so that their loads are in flight
+// together; the grid strides over the rows.
+#include "launch.hpp"
+#include "row_ops.hpp"
+
+namespace kvc {
+
+namespace {
+
+constexpr int kBlock = 256;                 // 4 waves
+constexpr int kWavesPerBlock = kBlock / kLanes;
+
+template <int L>
+__device__ __forceinline__ PagedKV<L> paged(const CacheView& c) {
+  return PagedKV<L>{c.base, c.page_stride, c.num_pages, c.page_bits};
+}
+
+__device__ __forceinline__ void raise_status(int32_t* status, int32_t bit) {
+  if (status != nullptr && lane_id() == 0) atomicOr(status, bit);
+}
+
+// ------------------------------------------------------------------ store
+template <int L>
+__global__ __launch_bounds__(kBlock) void store_rows_kernel(StoreParams p) {
+  const PagedKV<L> kv = paged<L>(p.cache);
+  const int lane = lane_id();
+  const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  for (int64_t i = wave0; i < p.n; i += nwaves) {
+    const uint4 x = ld_u4_nt(p.rows + i * p.row_stride + kDimsPerLane * lane);
+    const int64_t loc = uniform(p.out_loc[i]);
+    bool write = loc != 0;
+    if (write && !kv.valid(loc)) {
+      raise_status(p.status, kStPageRange);
+      write = false;
+    }
+    const int64_t slot = write ? loc : 0;
+    store_row_wave<L>(x, kv.data(slot), kv.scale(slot), write);
+  }
+}
+
+// ------------------------------------------------------------------ gather
+// rows handled together by one wave per loop trip
+constexpr int kGatherUnroll = 4;
+
+template <int L> struct LaneCodes;          // this lane's share of a row
+template <> struct LaneCodes<kV41> { uint2 codes; uint32_t scale; };
+template <> struct LaneCodes<kV41Fp4> { uint32_t codes; uint32_t scale; };
+template <> struct LaneCodes<kV4> { uint4 raw; uint32_t scale; };
+
+template <int L>
+__device__ __forceinline__ LaneCodes<L> load_lane(const PagedKV<L>& kv, int64_t slot, int lane);
+
+template <>
+__device__ __forceinline__ LaneCodes<kV41> load_lane<kV41>(const PagedKV<kV41>& kv, int64_t slot,
+                                                           int lane) {
+  LaneCodes<kV41> r;
+  const u32x2 c = __builtin_nontemporal_load((const u32x2*)(kv.data(slot) + 8 * lane));
+  r.codes = make_uint2(c.x, c.y);
+  r.scale = __builtin_nontemporal_load(kv.scale(slot) + (lane >> 2));
+  return r;
+}
+template <>
+__device__ __forceinline__ LaneCodes<kV41Fp4> load_lane<kV41Fp4>(const PagedKV<kV41Fp4>& kv,
+                                                                 int64_t slot, int lane) {
+  LaneCodes<kV41Fp4> r;
+  r.codes = __builtin_nontemporal_load((const uint32_t*)(kv.data(slot) + 4 * lane));
+  r.scale = __builtin_nontemporal_load(kv.scale(slot) + (lane >> 1));
+  return r;
+}
+template <>
+__device__ __forceinline__ LaneCodes<kV4> load_lane<kV4>(const PagedKV<kV4>& kv, int64_t slot,
+                                                         int lane) {
+  LaneCodes<kV4> r;
+  const uint8_t* d = kv.data(slot);
+  if (lane < kRopeLane0) {
+    const u32x2 c = __builtin_nontemporal_load((const u32x2*)(d + 8 * lane));
+    r.raw = make_uint4(c.x, c.y, 0u, 0u);
+    r.scale = __builtin_nontemporal_load(kv.scale(slot) + (lane >> 3));
+  } else {
+    r.raw = ld_u4_nt(d + kNope + 16 * (lane - kRopeLane0));
+    r.scale = 0;
+  }
+  return r;
+}
+
+template <int L>
+__device__ __forceinline__ uint4 decode_lane(const LaneCodes<L>& c, int lane);
+template <>
+__device__ __forceinline__ uint4 decode_lane<kV41>(const LaneCodes<kV41>& c, int) {
+  return dq_fp8x8(c.codes, (int)c.scale);
+}
+template <>
+__device__ __forceinline__ uint4 decode_lane<kV41Fp4>(const LaneCodes<kV41Fp4>& c, int) {
+  return dq_fp4x8(c.codes, c.scale);
+}
+template <>
+__device__ __forceinline__ uint4 decode_lane<kV4>(const LaneCodes<kV4>& c, int lane) {
+  if (lane >= kRopeLane0) return c.raw;
+  return dq_fp8x8(make_uint2(c.raw.x, c.raw.y), (int)c.scale);
+}
+
+template <int L>
+__global__ __launch_bounds__(kBlock) void dequant_gather_kernel(GatherParams p) {
+  const PagedKV<L> kv = paged<L>(p.cache);
+  const int lane = lane_id();
+  const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const int64_t page_mask = (int64_t(1) << p.cache.page_bits) - 1;
+
+  for (int64_t base = wave0 * kGatherUnroll; base < p.n; base += nwaves * kGatherUnroll) {
+    int64_t slot[kGatherUnroll];
+    bool live[kGatherUnroll];
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int64_t r = base + u;
+      const int64_t id = r < p.n ? (int64_t)uniform(p.ids[r]) : -1;
+      int64_t s = -1;
+      if (id >= 0) {
+        if (p.page_table != nullptr) {
+          const int64_t lp = id >> p.cache.page_bits;
+          if (lp < p.n_pages) {
+            const int64_t phys = uniform(p.page_table[lp]);
+            if (phys >= 0 && phys < kv.num_pages) {
+              s = (phys << p.cache.page_bits) | (id & page_mask);
+            } else {
+              raise_status(p.status, kStPageRange);
+            }
+          } else {
+            raise_status(p.status, kStIdRange);
+          }
+        } else if (kv.valid(id)) {
+          s = id;
+        } else {
+          raise_status(p.status, kStIdRange);
+        }
+      }
+      slot[u] = s;
+      live[u] = s >= 0;
+    }
+    LaneCodes<L> c[kGatherUnroll];
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u)
+      if (live[u]) c[u] = load_lane<L>(kv, slot[u], lane);
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int64_t r = base + u;
+      if (r >= p.n) break;
+      const uint4 o = live[u] ? decode_lane<L>(c[u], lane) : make_uint4(0u, 0u, 0u, 0u);
+      st_u4_nt(p.out + r * p.out_stride + kDimsPerLane * lane, o);
+    }
+  }
+}
+
+template <typename K, typename P>
+hipError_t launch(K kernel, int blocks, const P& p, hipStream_t stream) {
+  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kBlock), 0, stream, p);
+  return hipGetLastError();
+}
+
+int grid_for(int64_t units, int64_t per_block, int cap) {
+  int64_t b = (units + per_block - 1) / per_block;
+  if (b > cap) b = cap;
+  return (int)(b < 1 ? 1 : b);
+}
+
+}  // namespace
+
+LaunchTuning& launch_tuning() {
+  static LaunchTuning t{0, 0};
+  return t;
+}
+
+hipError_t launch_store_rows(const StoreParams& p, hipStream_t stream) {
+  const int blocks = grid_for(p.n, kWavesPerBlock, 8192);
+  switch (p.cache.layout) {
+    case kV41: return launch(store_rows_kernel<kV41>, blocks, p, stream);
+    case kV41Fp4: return launch(store_rows_kernel<kV41Fp4>, blocks, p, stream);
+    default: return launch(store_rows_kernel<kV4>, blocks, p, stream);
+  }
+}
+
+hipError_t launch_dequant_gather(const GatherParams& p, hipStream_t stream) {
+  int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * kGatherUnroll, 4096);
+  if (launch_tuning().gather_blocks > 0) blocks = launch_tuning().gather_blocks;
+  switch (p.cache.layout) {
+    case kV41: return launch(dequant_gather_kernel<kV41>, blocks, p, stream);
+    case kV41Fp4: return launch(dequant_gather_kernel<kV41Fp4>, blocks, p, stream);
+    default: return launch(dequant_gather_kernel<kV4>, blocks, p, stream);
+  }
+}
+
+}  // namespace kvc

@@ -1,0 +1,178 @@
+"""The C-ABI library: it loads, exports every symbol include/kvc.h declares,
+and its host-side checks and reuse head behave as documented.  No GPU: only
+calls that return before any launch are made."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(kvc_[a-z_0-9]+)\s*\(", src)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def kvc():
+    import fp8_fp4_quantized_amd as k
+    return k
+
+
+def test_every_declared_symbol_is_exported(kvc):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(kvc.lib(), n), n
+    # the binding covers the same list
+    assert set(names) == set(kvc.SIGNATURES)
+
+
+def test_version_and_layouts(kvc):
+    assert kvc.kvc_version() == 1
+    want = {"V4": (576, 8, 584, 64, 448), "V41": (512, 16, 528, 32, 512),
+            "V41_FP4": (256, 32, 288, 16, 512)}
+    for name, w in want.items():
+        i = kvc.kvc_layout_query(name)
+        assert (i.data_bytes, i.scale_bytes, i.row_bytes, i.group, i.quant_dims) == w
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_layout_query(7)
+    assert e.value.code == kvc.KVC_EUNSUPPORTED
+
+
+def test_layouts_agree_with_oracle(kvc):
+    import oracle
+    for name in ("V4", "V41", "V41_FP4"):
+        i = kvc.kvc_layout_query(name)
+        assert oracle.layout_bytes(name) == (i.data_bytes, i.scale_bytes, i.row_bytes, i.group)
+
+
+FAKE = 0x7F0000000000   # never dereferenced: every call below returns before a launch
+
+
+def _cache(kvc, layout=1, page_size=64, stride=None, pages=4, base=FAKE):
+    rb = kvc.kvc_layout_query(layout).row_bytes if layout in (0, 1, 2) else 1024
+    return kvc.kvc_cache(base, layout, page_size,
+                         page_size * rb if stride is None else stride, pages)
+
+
+def test_cache_descriptor_checks(kvc):
+    L = kvc.lib()
+    bad = [
+        _cache(kvc, base=0),                      # NULL
+        _cache(kvc, base=FAKE + 8),               # misaligned
+        _cache(kvc, page_size=48),                # not a power of two
+        _cache(kvc, page_size=8192),              # too large
+        _cache(kvc, stride=64 * 528 - 16),        # too small a page stride
+        _cache(kvc, stride=64 * 528 + 8),         # not a multiple of 16
+        _cache(kvc, pages=0),
+    ]
+    for c in bad:
+        rc = L.kvc_store_rows(C.byref(c), FAKE, 512, FAKE, 1, None, None)
+        assert rc == kvc.KVC_EINVAL, kvc.kvc_last_error()
+        assert kvc.kvc_last_error()
+    c = _cache(kvc, layout=9)
+    assert L.kvc_store_rows(C.byref(c), FAKE, 512, FAKE, 1, None, None) == kvc.KVC_EUNSUPPORTED
+    assert L.kvc_store_rows(None, FAKE, 512, FAKE, 1, None, None) == kvc.KVC_EINVAL
+
+
+def test_store_and_gather_argument_checks(kvc):
+    L = kvc.lib()
+    c = _cache(kvc)
+    assert L.kvc_store_rows(C.byref(c), FAKE, 512, FAKE, 0, None, None) == kvc.KVC_OK  # n = 0
+    assert kvc.kvc_last_error() == ""
+    assert L.kvc_store_rows(C.byref(c), FAKE, 512, FAKE, -1, None, None) == kvc.KVC_EINVAL
+    assert L.kvc_store_rows(C.byref(c), None, 512, FAKE, 3, None, None) == kvc.KVC_EINVAL
+    assert L.kvc_store_rows(C.byref(c), FAKE, 500, FAKE, 3, None, None) == kvc.KVC_EINVAL
+    assert L.kvc_store_rows(C.byref(c), FAKE + 2, 512, FAKE, 3, None, None) == kvc.KVC_EINVAL
+    assert L.kvc_dequant_gather(C.byref(c), None, 0, FAKE, 0, FAKE, 512, None, None) == kvc.KVC_OK
+    assert L.kvc_dequant_gather(C.byref(c), None, 0, None, 5, FAKE, 512, None, None) == kvc.KVC_EINVAL
+    assert L.kvc_dequant_gather(C.byref(c), FAKE, 0, FAKE, 5, FAKE, 512, None, None) == kvc.KVC_EINVAL
+    assert L.kvc_dequant_gather(C.byref(c), None, 0, FAKE, 5, FAKE, 500, None, None) == kvc.KVC_EINVAL
+    assert L.kvc_dequant_gather(C.byref(c), None, 0, FAKE, 5, FAKE + 8, 512, None, None) == kvc.KVC_EINVAL
+
+
+def _args(kvc, **kw):
+    a = kvc.kvc_compress_args()
+    a.ratio, a.mode = 2, kvc.MODE_PREFILL
+    a.kv, a.kv_stride, a.score, a.score_stride = FAKE, 1024, FAKE + 1024, 1024
+    a.num_slots = 4
+    a.offsets, a.start_pos, a.page_table, a.pt_stride = FAKE, FAKE, FAKE, 8
+    a.state, a.norm_w, a.eps, a.freqs, a.max_pos = FAKE, FAKE, 1e-6, FAKE, 100
+    a.latent_out, a.latent_stride, a.max_out_rows = FAKE, 512, 10
+    a.cache = _cache(kvc, layout=2, page_size=128)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_compress_argument_checks(kvc):
+    L = kvc.lib()
+    bad_inval = [
+        dict(kv=0), dict(kv_stride=500), dict(kv=FAKE + 4), dict(score=0), dict(score_stride=4),
+        dict(state=0), dict(offsets=0), dict(start_pos=0), dict(page_table=0),
+        dict(pt_stride=0), dict(norm_w=0), dict(freqs=0), dict(max_pos=0), dict(latent_out=0),
+        dict(latent_stride=256), dict(max_out_rows=-1), dict(num_slots=-1),
+        dict(num_slots=8192), dict(eps=-1.0), dict(prequant_out=FAKE, prequant_stride=3),
+    ]
+    for kw in bad_inval:
+        a = _args(kvc, **kw)
+        assert L.kvc_compress_store(C.byref(a), None) == kvc.KVC_EINVAL, kw
+    for kw in (dict(ratio=3), dict(ratio=0), dict(mode=5)):
+        a = _args(kvc, **kw)
+        assert L.kvc_compress_store(C.byref(a), None) == kvc.KVC_EUNSUPPORTED, kw
+    # decode needs out_loc or a page table
+    a = _args(kvc, mode=kvc.MODE_DECODE, page_table=0, out_loc=0)
+    assert L.kvc_compress_store(C.byref(a), None) == kvc.KVC_EINVAL
+    # nothing to do is fine
+    a = _args(kvc, num_slots=0)
+    assert L.kvc_compress_store(C.byref(a), None) == kvc.KVC_OK
+    assert L.kvc_compress_store(None, None) == kvc.KVC_EINVAL
+
+
+def test_reuse_head_semantics(kvc):
+    """Head reuse (sglang PR #45909, summary): same (source cache, ids, row
+    count) hits; a plain get (forget), a reallocation (new output or cache
+    pointer) or a new forward forgets the head.  n = 0 keeps every call off
+    the GPU, the key logic is the same."""
+    L = kvc.lib()
+    kb = L.kvc_kvbuf_create()
+    assert kb
+    c = _cache(kvc)
+    hit = C.c_int32(-1)
+
+    def call(cache=c, pt=None, ids=FAKE, n=0, out=FAKE, stride=512):
+        rc = L.kvc_dequant_gather_reuse(kb, C.byref(cache), pt, 0 if pt is None else 16, ids, n,
+                                        out, stride, None, C.byref(hit), None)
+        assert rc == kvc.KVC_OK
+        return hit.value
+
+    assert call() == 0
+    assert call() == 1
+    assert call() == 1
+    assert call(ids=FAKE + 64) == 0          # other ids
+    assert call(ids=FAKE + 64) == 1
+    assert call(out=FAKE + 4096) == 0        # output reallocated
+    assert call(out=FAKE + 4096) == 1
+    L.kvc_kvbuf_forget(kb)                   # a plain get
+    assert call(out=FAKE + 4096) == 0
+    L.kvc_kvbuf_begin_forward(kb)            # a new forward
+    assert call(out=FAKE + 4096) == 0
+    assert call(out=FAKE + 4096) == 1
+    c2 = _cache(kvc, base=FAKE + 1 << 20)    # another source cache
+    assert call(cache=c2, out=FAKE + 4096) == 0
+    assert call(cache=c2, pt=FAKE, out=FAKE + 4096) == 0   # with a page table
+    assert call(cache=c2, pt=FAKE, out=FAKE + 4096) == 1
+    assert call(cache=c2, pt=FAKE, out=FAKE + 4096, stride=1024) == 0
+    # a failed call leaves no head
+    bad = _cache(kvc, page_size=3)
+    rc = L.kvc_dequant_gather_reuse(kb, C.byref(bad), None, 0, FAKE, 0, FAKE, 512, None,
+                                    C.byref(hit), None)
+    assert rc == kvc.KVC_EINVAL and hit.value == 0
+    assert call(cache=c2, pt=FAKE, out=FAKE + 4096, stride=1024) == 0
+    L.kvc_kvbuf_destroy(kb)
