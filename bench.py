@@ -203,7 +203,7 @@ def main() -> int:
         m = 65536
         ids_sub = c4["ids"][:m]
         reps, spent, done_rows = 0, 0.0, 0
-        while spent < 10.0 and reps < 20:
+        while spent < 10.0 and reps < 400:
             cache_h = np.zeros((c3["num_pages"], 128 * fp4.row_bytes), np.uint8)
             t = time.perf_counter()
             oracle.compress(ratio=2, mode=oracle.PREFILL, kv=c3["kv"][:n4], fused=True,

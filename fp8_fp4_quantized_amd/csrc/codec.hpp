@@ -21,13 +21,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
 // |x| ordering of finite bf16 values equals the integer ordering of their
-// low 15 bits, so a group's amax is an integer max
+// low 15 bits, so a group's amax is an integer max.  The four words each hold
+// two bf16; the maxima are taken per 16-bit half (v_pk_max_u16).
 __device__ __forceinline__ uint32_t absmax_bf16x8(uint4 x) {
   const uint32_t m = 0x7FFF7FFFu;
-  uint32_t a = max(x.x & m, x.y & m), b = max(x.z & m, x.w & m);
-  uint32_t c = max(a, b);                  // two lane-wise maxima, lo and hi halves
-  return max(c & 0xFFFFu, c >> 16);
+  const u16x2 a = __builtin_bit_cast(u16x2, x.x & m), b = __builtin_bit_cast(u16x2, x.y & m);
+  const u16x2 c = __builtin_bit_cast(u16x2, x.z & m), d = __builtin_bit_cast(u16x2, x.w & m);
+  const u16x2 e = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                            __builtin_elementwise_max(c, d));
+  return max((uint32_t)e.x, (uint32_t)e.y);
 }
 
 // ue8m0 scale exponent of a group from the fp32 bits of its amax: the

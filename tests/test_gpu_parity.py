@@ -219,7 +219,7 @@ def _run_compress(K, case, layout, ratio, mode, fused=True, eps=None, max_out_ro
     dc = dev(hc)
     state_h = case["state"].copy()
     state_d = dev(case["state"])
-    pt = case["page_table"] if page_table == "case" else page_table
+    pt = case["page_table"] if isinstance(page_table, str) else page_table
     start = case["start_pos"] if mode == oracle.PREFILL else case["pos"]
     kv = case["kv"]
     if fused:
