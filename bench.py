@@ -69,6 +69,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gather-blocks", type=int, default=0)
     ap.add_argument("--compress-blocks", type=int, default=0)
+    ap.add_argument("--compress-tile-rows", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path runs on one GPU's share); "
@@ -83,7 +84,7 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    kvc.kvc_set_launch_shape(args.gather_blocks, args.compress_blocks)
+    kvc.kvc_set_launch_shape(args.gather_blocks, args.compress_blocks, args.compress_tile_rows)
 
     def d(a):
         a = np.ascontiguousarray(a)
@@ -111,31 +112,34 @@ def main() -> int:
     g_cache = kvc.Cache(d(c4["cache"]), "V41", 64)
     g_pt, g_ids = d(c4["page_table"]), d(c4["ids"])
     n_ids = int(c4["ids"].size)
-    g_out = torch.empty((n_ids, 512), dtype=torch.int16, device=dev)
+    # three output buffers used in turn: a step never rewrites the lines the
+    # previous step left in the 256 MB Infinity Cache, so the gather's writes
+    # reach HBM as they would in a forward pass (cold, not cache-absorbed)
+    g_outs = [torch.empty((n_ids, 512), dtype=torch.int16, device=dev) for _ in range(3)]
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(k, ev=None):
         if ev is not None:
             ev[0].record(stream)
         kvc.kvc_compress_store(**c3_args, status=status)
         if ev is not None:
             ev[1].record(stream)
-        kvc.kvc_dequant_gather(g_cache, g_pt, g_ids, g_out, status)
+        kvc.kvc_dequant_gather(g_cache, g_pt, g_ids, g_outs[k % 3], status)
         if ev is not None:
             ev[2].record(stream)
 
     # ---------------------------------------------------------------- timing
-    for _ in range(args.warmup):
-        step()
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
     assert int(status.item()) == 0, f"device status {int(status.item())}"
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
-        step(events[k])
+        step(k, events[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     comp_ms = [e[0].elapsed_time(e[1]) for e in events]

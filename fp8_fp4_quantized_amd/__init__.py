@@ -76,7 +76,7 @@ SIGNATURES = {
                                            _I64, _VP, _VP, _VP]),
     "kvc_last_error": (C.c_char_p, []),
     "kvc_version": (C.c_int, []),
-    "kvc_set_launch_shape": (C.c_int, [_I32, _I32]),
+    "kvc_set_launch_shape": (C.c_int, [_I32, _I32, _I32]),
 }
 
 _lib = None
@@ -146,8 +146,9 @@ def kvc_layout_query(layout) -> kvc_layout_info:
     return info
 
 
-def kvc_set_launch_shape(gather_blocks: int = 0, compress_blocks: int = 0) -> None:
-    _check(lib().kvc_set_launch_shape(gather_blocks, compress_blocks))
+def kvc_set_launch_shape(gather_blocks: int = 0, compress_blocks: int = 0,
+                         compress_tile_rows: int = 0) -> None:
+    _check(lib().kvc_set_launch_shape(gather_blocks, compress_blocks, compress_tile_rows))
 
 
 def kvc_store_rows(cache: Cache, rows: torch.Tensor, out_loc: torch.Tensor,

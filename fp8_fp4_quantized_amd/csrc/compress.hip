@@ -1,17 +1,19 @@
 // compress.hip -- the fused ratio-1 / ratio-2 compressor (gfx950).
 //
-// One 64-lane wave makes one compressed row: it loads the pair's kv and score
-// rows (16 B per lane each), pools them with a per-dim softmax over the two
-// scores (ratio 2), RMS-normalises over the 512 dims (one wave sum), writes
-// the pre-RoPE latent, rotates the 64 rope dims (lanes 56..63, four pairs per
-// lane, no cross-lane traffic), rounds to bf16 and quantizes the row into its
-// paged slot.  (sglang PR #39652 "dsv4.1: compression, KV I/O, and metadata
-// kernels", Summary and Review; sglang PR #46230, summary.)
+// One 64-lane wave makes one compressed row at a time: it loads the pair's kv
+// and score rows (16 B per lane each), pools them with a per-dim softmax over
+// the two scores (ratio 2), RMS-normalises over the 512 dims (one wave sum),
+// writes the pre-RoPE latent, rotates the 64 rope dims (lanes 56..63, four
+// pairs per lane, no cross-lane traffic), rounds to bf16 and quantizes the row
+// into its paged slot.  (sglang PR #39652 "dsv4.1: compression, KV I/O, and
+// metadata kernels", Summary and Review; sglang PR #46230, summary.)
 //
 // Prefill batches are ragged: each workgroup turns the int32 [2, S] extend
 // offsets into per-slot work and latent starts with a scan in LDS, then its
 // waves look their work items up by binary search, so the launch needs no
-// host-side knowledge of the row counts (and can be captured in a graph).
+// host-side knowledge of the row counts (and can be captured in a graph).  A
+// work item is a tile of consecutive compressed rows of one slot; a wave
+// issues the loads of all its rows before it finishes the first.
 #include "launch.hpp"
 #include "row_ops.hpp"
 
@@ -22,53 +24,74 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kLanes;
 constexpr int kMaxPrefillSlots = 8191;   // two LDS tables of S + 1 ints fit in 64 KiB
+constexpr int kTileLog2 = 1;             // default: 2 consecutive compressed rows per work item
 
 __device__ __forceinline__ void raise_status(int32_t* status, int32_t bit) {
   if (status != nullptr && lane_id() == 0) atomicOr(status, bit);
 }
 
+// One compressed row.  Token rows are indices into the projection buffer;
+// `from_state` says the pair's first token is the slot's pending state.
 struct RowJob {
-  const uint16_t* k0;     // first token of the pair (ratio 2)
-  const uint16_t* s0;
-  const uint16_t* k1;     // second (or only) token
-  const uint16_t* s1;
+  int64_t t1;             // second (or only) token of the row
   int64_t rot_pos;        // rotary position
-  int64_t c;              // compressed row index within the slot
-  int32_t slot;
   int64_t latent_idx;
+  int64_t loc;            // destination slot in the cache (0: no write)
+  int32_t slot;
+  int32_t loc_err;        // status bit raised instead of the write (0: none)
+  bool from_state;
 };
 
-template <int L, int RATIO, int MODE>
-__device__ __forceinline__ void compress_row(const CompressParams& p, const PagedKV<L>& kv,
-                                             const float (&w)[8], const RowJob& j) {
+// registers of one row's inputs: this lane's 16 B of the pair's kv and score
+// rows and (rope lanes) its 8 rotary-table entries
+struct RowIn {
+  uint4 k0, s0, k1, s1;
+  float4 f0, f1;
+};
+
+// Every lane issues the same loads whatever the row (the first token comes
+// from the pending state or the buffer by an address select, and the lanes
+// that hold no rope dims read a rope lane's table entries), so the count of
+// memory operations in flight is fixed and the compiler's waits stay exact.
+template <int RATIO>
+__device__ __forceinline__ RowIn load_row(const CompressParams& p, const RowJob& j) {
+  const int lane = lane_id();
+  const int dim0 = kDimsPerLane * lane;
+  RowIn in;
+  in.k1 = ld_u4_nt(p.kv + j.t1 * p.kv_stride + dim0);
+  in.k0 = in.s0 = in.s1 = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (RATIO == 2) {
+    in.s1 = ld_u4_nt(p.score + j.t1 * p.score_stride + dim0);
+    const uint16_t* st = p.state + (int64_t)j.slot * 2 * kDim;
+    const uint16_t* k0 = j.from_state ? st : p.kv + (j.t1 - 1) * p.kv_stride;
+    const uint16_t* s0 = j.from_state ? st + kDim : p.score + (j.t1 - 1) * p.score_stride;
+    in.k0 = ld_u4(k0 + dim0);
+    in.s0 = ld_u4(s0 + dim0);
+  }
+  const int64_t rp = j.rot_pos < 0 ? 0 : (j.rot_pos >= p.max_pos ? p.max_pos - 1 : j.rot_pos);
+  const float* fr = p.freqs + rp * kRope + kDimsPerLane * ((lane - kRopeLane0) & 7);
+  in.f0 = *(const float4*)fr;
+  in.f1 = *(const float4*)(fr + 4);
+  return in;
+}
+
+template <int L, int RATIO>
+__device__ __forceinline__ void finish_row(const CompressParams& p, const PagedKV<L>& kv,
+                                           const float (&w)[8], const RowJob& j, const RowIn& in) {
   const int lane = lane_id();
   if (j.rot_pos < 0 || j.rot_pos >= p.max_pos) {
     raise_status(p.status, kStPosRange);
     return;
   }
-  // ---- loads: the pair's rows and this lane's slice of the rotary table
   const int dim0 = kDimsPerLane * lane;
-  const uint4 xk1 = ld_u4_nt(j.k1 + dim0);
-  uint4 xk0 = make_uint4(0u, 0u, 0u, 0u), xs0 = xk0, xs1 = xk0;
-  if constexpr (RATIO == 2) {
-    xk0 = ld_u4_nt(j.k0 + dim0);
-    xs0 = ld_u4_nt(j.s0 + dim0);
-    xs1 = ld_u4_nt(j.s1 + dim0);
-  }
-  float4 f0 = make_float4(1.f, 0.f, 1.f, 0.f), f1 = f0;
-  if (lane >= kRopeLane0) {
-    const float* fr = p.freqs + j.rot_pos * kRope + kDimsPerLane * (lane - kRopeLane0);
-    f0 = *(const float4*)fr;
-    f1 = *(const float4*)(fr + 4);
-  }
 
   // ---- pooling (ratio 2): softmax over the two scores, per dim
-  const uint32_t k1w[4] = {xk1.x, xk1.y, xk1.z, xk1.w};
+  const uint32_t k1w[4] = {in.k1.x, in.k1.y, in.k1.z, in.k1.w};
   float v[8];
   if constexpr (RATIO == 2) {
-    const uint32_t k0w[4] = {xk0.x, xk0.y, xk0.z, xk0.w};
-    const uint32_t s0w[4] = {xs0.x, xs0.y, xs0.z, xs0.w};
-    const uint32_t s1w[4] = {xs1.x, xs1.y, xs1.z, xs1.w};
+    const uint32_t k0w[4] = {in.k0.x, in.k0.y, in.k0.z, in.k0.w};
+    const uint32_t s0w[4] = {in.s0.x, in.s0.y, in.s0.z, in.s0.w};
+    const uint32_t s1w[4] = {in.s1.x, in.s1.y, in.s1.z, in.s1.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -77,9 +100,11 @@ __device__ __forceinline__ void compress_row(const CompressParams& p, const Page
         const float a1 = h ? bf16_hi(s1w[q]) : bf16_lo(s1w[q]);
         const float kk0 = h ? bf16_hi(k0w[q]) : bf16_lo(k0w[q]);
         const float kk1 = h ? bf16_hi(k1w[q]) : bf16_lo(k1w[q]);
-        const float m = fmaxf(a0, a1);
-        const float e0 = __expf(a0 - m), e1 = __expf(a1 - m);
-        v[2 * q + h] = (e0 * kk0 + e1 * kk1) * __builtin_amdgcn_rcpf(e0 + e1);
+        // the two-way softmax is a sigmoid of the score difference:
+        // v = k1 + (k0 - k1) / (1 + exp(a1 - a0)); exp overflowing to
+        // infinity gives weight 0, underflowing to 0 gives weight 1
+        const float g = __builtin_amdgcn_rcpf(1.f + __expf(a1 - a0));
+        v[2 * q + h] = fmaf(kk0 - kk1, g, kk1);
       }
     }
   } else {
@@ -113,7 +138,7 @@ __device__ __forceinline__ void compress_row(const CompressParams& p, const Page
   // ---- RoPE on the last 64 dims: pairs (2i, 2i+1) times (cos, sin)
   uint4 z = lat;
   if (lane >= kRopeLane0) {
-    const float cs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+    const float cs[8] = {in.f0.x, in.f0.y, in.f0.z, in.f0.w, in.f1.x, in.f1.y, in.f1.z, in.f1.w};
     float o[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -126,35 +151,33 @@ __device__ __forceinline__ void compress_row(const CompressParams& p, const Page
   }
   if (p.prequant != nullptr && lat_ok) st_u4(p.prequant + j.latent_idx * p.prequant_stride + dim0, z);
 
-  // ---- destination slot (out_loc == 0: padded row, no write)
-  int64_t loc;
-  bool write = true;
-  if (MODE == 1 && p.out_loc != nullptr) {
-    loc = uniform(p.out_loc[j.slot]);
-  } else {
-    const int64_t lp = j.c >> p.cache.page_bits;
-    if (lp >= p.pt_stride) {
-      raise_status(p.status, kStPtRange);
-      write = false;
-      loc = 0;
-    } else {
-      const int64_t phys = uniform(p.page_table[(int64_t)j.slot * p.pt_stride + lp]);
-      if (phys < 0 || phys >= kv.num_pages) {
-        raise_status(p.status, kStPageRange);
-        write = false;
-        loc = 0;
-      } else {
-        loc = (phys << p.cache.page_bits) | (j.c & ((int64_t(1) << p.cache.page_bits) - 1));
-      }
-    }
-  }
-  if (write && loc == 0) write = false;
-  if (write && !kv.valid(loc)) {
+  // ---- quantized store at the destination slot (0: padded row, no write)
+  bool write = j.loc_err == 0 && j.loc != 0;
+  if (j.loc_err != 0) raise_status(p.status, j.loc_err);
+  if (write && !kv.valid(j.loc)) {
     raise_status(p.status, kStPageRange);
     write = false;
   }
-  const int64_t slot = write ? loc : 0;
+  const int64_t slot = write ? j.loc : 0;
   store_row_wave<L>(z, kv.data(slot), kv.scale(slot), write);
+}
+
+// the destination slot of row c of slot b through the page table
+__device__ __forceinline__ void page_loc(const CompressParams& p, int32_t b, int64_t c,
+                                         int64_t& loc, int32_t& err) {
+  loc = 0;
+  err = 0;
+  const int64_t lp = c >> p.cache.page_bits;
+  if (lp >= p.pt_stride) {
+    err = kStPtRange;
+    return;
+  }
+  const int64_t phys = ld_ro(p.page_table + (int64_t)b * p.pt_stride + lp);
+  if (phys < 0 || phys >= p.cache.num_pages) {
+    err = kStPageRange;
+    return;
+  }
+  loc = (phys << p.cache.page_bits) | (c & ((int64_t(1) << p.cache.page_bits) - 1));
 }
 
 // copy a token's kv and score rows into the slot's pending state
@@ -167,24 +190,33 @@ __device__ __forceinline__ void write_state(const CompressParams& p, int32_t b, 
   st_u4(st + kDim + dim0, scv);
 }
 
-// per-slot work of a prefill batch: compressed rows, and whether the last
-// token becomes the pending state (ratio 2); a slot with a tail and rows does
-// the tail in its first work item, after that item has read the old state
+// Per-slot work of a prefill batch.  The slot's compressed rows c0 .. c0 +
+// rows - 1 are cut into tiles aligned to multiples of T in c, so every tile
+// stays inside one page (T divides the page size) and the rows that share a
+// scale cache line are written by one wave.  A last token at an even
+// position becomes the pending state (ratio 2); the slot's first tile does
+// that after its first row, which may read the old state.  A slot with such a
+// tail and no rows gets one work item for it.
 struct SlotWork {
-  int32_t rows, items;
+  int32_t rows, items, c0;
   bool tail;
 };
 template <int RATIO>
-__device__ __forceinline__ SlotWork slot_work(int32_t n, int32_t P) {
-  SlotWork s{0, 0, false};
+__device__ __forceinline__ SlotWork slot_work(int32_t n, int32_t P, int32_t tile_log2) {
+  SlotWork s{0, 0, 0, false};
   if (n <= 0 || P < 0) return s;
   if constexpr (RATIO == 1) {
     s.rows = n;
-    s.items = n;
+    s.c0 = P;
   } else {
     s.rows = ((P + n) >> 1) - (P >> 1);      // odd positions in [P, P + n)
+    s.c0 = P >> 1;                           // row of the first odd position
     s.tail = ((P + n) & 1) != 0;             // last position P + n - 1 is even
-    s.items = s.rows > 0 ? s.rows : (s.tail ? 1 : 0);
+  }
+  if (s.rows > 0) {
+    s.items = ((s.c0 + s.rows - 1) >> tile_log2) - (s.c0 >> tile_log2) + 1;
+  } else {
+    s.items = s.tail ? 1 : 0;
   }
   return s;
 }
@@ -198,8 +230,8 @@ __device__ void build_tables(const CompressParams& p, int32_t* item_start, int32
   int32_t carry_i = 0, carry_r = 0;
   for (int base = 0; base < S; base += kBlock) {
     const int b = base + threadIdx.x;
-    SlotWork sw{0, 0, false};
-    if (b < S) sw = slot_work<RATIO>(p.offsets[S + b], p.start_pos[b]);
+    SlotWork sw{0, 0, 0, false};
+    if (b < S) sw = slot_work<RATIO>(p.offsets[S + b], p.start_pos[b], p.tile_log2);
     int32_t si = sw.items, sr = sw.rows;
 #pragma unroll
     for (int d = 1; d < kLanes; d <<= 1) {
@@ -236,8 +268,104 @@ __device__ void build_tables(const CompressParams& p, int32_t* item_start, int32
   __syncthreads();
 }
 
-template <int L, int RATIO, int MODE>
-__global__ __launch_bounds__(kBlock) void compress_kernel(CompressParams p) {
+// One prefill work item: the tile kt of slot b (slot data already at hand).
+template <int L, int RATIO, int kTileRows>
+__device__ __forceinline__ void run_tile(const CompressParams& p, const PagedKV<L>& kv,
+                                         const float (&w)[8], int32_t b, int64_t kt, int64_t lat0,
+                                         int64_t rows, int64_t first, int32_t n, int64_t P) {
+  const int tl = p.tile_log2;
+  const int64_t page_mask = (int64_t(1) << p.cache.page_bits) - 1;
+  const int64_t c0 = RATIO == 1 ? P : (P >> 1);
+  const int64_t tbase = ((c0 >> tl) + kt) << tl;
+  const int64_t c_lo = c0 > tbase ? c0 : tbase;
+  const int64_t c_end = c0 + rows, t_end = tbase + (int64_t(1) << tl);
+  const int64_t c_hi = c_end < t_end ? c_end : t_end;
+
+  if (c_lo < c_hi) {
+    // all loads of the tile's rows are issued before the first row is
+    // finished; a tile shorter than kTileRows reloads its last row
+    RowJob j[kTileRows];
+    RowIn in[kTileRows];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
+      const int64_t c = c_lo + r < c_hi ? c_lo + r : c_hi - 1;
+      j[r].slot = b;
+      j[r].latent_idx = lat0 + (c - c0);
+      if constexpr (RATIO == 1) {
+        j[r].t1 = first + (c - P);
+        j[r].rot_pos = c;
+        j[r].from_state = false;
+      } else {
+        const int64_t q = 2 * c + 1;             // odd position closing the pair
+        j[r].t1 = first + (q - P);
+        j[r].rot_pos = q - 1;
+        j[r].from_state = q - 1 < P;             // first token precedes the extend
+      }
+      in[r] = load_row<RATIO>(p, j[r]);
+    }
+    // the tile's rows share one page (aligned, no larger than a page): one
+    // page-table lookup, needed only when the rows are stored
+    int64_t loc0;
+    int32_t loc_err;
+    page_loc(p, b, c_lo, loc0, loc_err);
+    const int64_t page_base = loc0 - (c_lo & page_mask);
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) {
+      j[r].loc_err = loc_err;
+      j[r].loc = loc_err ? 0 : page_base + ((c_lo + r) & page_mask);
+      if (c_lo + r < c_hi) finish_row<L, RATIO>(p, kv, w, j[r], in[r]);
+    }
+  }
+  if constexpr (RATIO == 2) {
+    if (kt == 0 && ((P + n) & 1)) write_state(p, b, first + n - 1);
+  }
+}
+
+// Prefill with up to 64 slots: every lane holds one slot's work counts and
+// their inclusive prefix sums, and a work item finds its slot with one
+// ballot -- no LDS, no barrier.
+template <int L, int RATIO, int kTileRows>
+__global__ __launch_bounds__(kBlock) void compress_prefill_small_kernel(CompressParams p) {
+  const PagedKV<L> kv{p.cache.base, p.cache.page_stride, p.cache.num_pages, p.cache.page_bits};
+  const int lane = lane_id();
+  const int S = p.num_slots;
+  int32_t first = 0, n = 0, P = 0;
+  if (lane < S) {
+    first = p.offsets[lane];
+    n = p.offsets[S + lane];
+    P = p.start_pos[lane];
+  }
+  const uint4 wr = ld_u4(p.norm_w + kDimsPerLane * lane);
+  const SlotWork sw = lane < S ? slot_work<RATIO>(n, P, p.tile_log2) : SlotWork{0, 0, 0, false};
+  int32_t inc_i = sw.items, inc_r = sw.rows;
+#pragma unroll
+  for (int d = 1; d < kLanes; d <<= 1) {
+    const int32_t ti = __shfl_up(inc_i, d), tr = __shfl_up(inc_r, d);
+    if (lane >= d) {
+      inc_i += ti;
+      inc_r += tr;
+    }
+  }
+  const float w[8] = {bf16_lo(wr.x), bf16_hi(wr.x), bf16_lo(wr.y), bf16_hi(wr.y),
+                      bf16_lo(wr.z), bf16_hi(wr.z), bf16_lo(wr.w), bf16_hi(wr.w)};
+  const int64_t total = __builtin_amdgcn_readlane(inc_i, kLanes - 1);
+  const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  for (int64_t item = wave0; item < total; item += nwaves) {
+    // slot b = number of slots whose items all come before this one
+    const int32_t b = __builtin_popcountll(__ballot(inc_i <= item));
+    const int64_t kt = item - (__builtin_amdgcn_readlane(inc_i, b) - __builtin_amdgcn_readlane(sw.items, b));
+    const int64_t rows = __builtin_amdgcn_readlane(sw.rows, b);
+    const int64_t lat0 = __builtin_amdgcn_readlane(inc_r, b) - rows;
+    run_tile<L, RATIO, kTileRows>(p, kv, w, b, kt, lat0, rows, __builtin_amdgcn_readlane(first, b),
+                                  __builtin_amdgcn_readlane(n, b), __builtin_amdgcn_readlane(P, b));
+  }
+}
+
+// Prefill with any number of slots (up to kMaxPrefillSlots): the per-slot
+// prefix sums go to LDS and work items find their slot by binary search.
+template <int L, int RATIO, int kTileRows>
+__global__ __launch_bounds__(kBlock) void compress_prefill_kernel(CompressParams p) {
   extern __shared__ int32_t tables[];
   const PagedKV<L> kv{p.cache.base, p.cache.page_stride, p.cache.num_pages, p.cache.page_bits};
   const int lane = lane_id();
@@ -248,114 +376,105 @@ __global__ __launch_bounds__(kBlock) void compress_kernel(CompressParams p) {
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const int S = p.num_slots;
 
-  if constexpr (MODE == 0) {
-    int32_t* item_start = tables;
-    int32_t* row_start = tables + (S + 1);
-    build_tables<RATIO>(p, item_start, row_start);
-    const int64_t total = item_start[S];
-    for (int64_t item = wave0; item < total; item += nwaves) {
-      int lo = 0, hi = S;                        // item_start[lo] <= item < item_start[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (item_start[mid] <= item) lo = mid; else hi = mid;
-      }
-      const int32_t b = uniform(lo);
-      const int64_t k = item - uniform(item_start[b]);
-      const int32_t rows = uniform(row_start[b + 1]) - uniform(row_start[b]);
-      const int64_t first = uniform(p.offsets[b]);
-      const int32_t n = uniform(p.offsets[S + b]);
-      const int64_t P = uniform(p.start_pos[b]);
-      RowJob j;
-      j.slot = b;
-      j.latent_idx = uniform(row_start[b]) + k;
-      if constexpr (RATIO == 1) {
-        j.k0 = j.s0 = nullptr;
-        j.k1 = p.kv + (first + k) * p.kv_stride;
-        j.s1 = nullptr;
-        j.c = P + k;
-        j.rot_pos = P + k;
-        compress_row<L, RATIO, MODE>(p, kv, w, j);
-      } else {
-        if (k < rows) {
-          const int64_t q = (P | 1) + 2 * k;     // odd position closing the pair
-          const int64_t t1 = first + (q - P);
-          j.k1 = p.kv + t1 * p.kv_stride;
-          j.s1 = p.score + t1 * p.score_stride;
-          if (q - 1 >= P) {
-            j.k0 = j.k1 - p.kv_stride;
-            j.s0 = j.s1 - p.score_stride;
-          } else {                               // first token is the pending state
-            j.k0 = p.state + (int64_t)b * 2 * kDim;
-            j.s0 = j.k0 + kDim;
-          }
-          j.c = q >> 1;
-          j.rot_pos = q - 1;
-          compress_row<L, RATIO, MODE>(p, kv, w, j);
-        }
-        if (k == 0 && ((P + n) & 1)) write_state(p, b, first + n - 1);
-      }
+  int32_t* item_start = tables;
+  int32_t* row_start = tables + (S + 1);
+  build_tables<RATIO>(p, item_start, row_start);
+  const int64_t total = uniform(item_start[S]);
+
+  for (int64_t item = wave0; item < total; item += nwaves) {
+    int lo = 0, hi = S;                          // item_start[lo] <= item < item_start[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (uniform(item_start[mid]) <= item) lo = mid; else hi = mid;
     }
-  } else {
-    const int64_t b64 = wave0;
-    if (b64 >= S) return;
-    const int32_t b = (int32_t)b64;
-    const int64_t pos = uniform(p.start_pos[b]);
-    if (pos < 0) return;
-    RowJob j;
-    j.slot = b;
-    j.latent_idx = b;
-    j.k1 = p.kv + (int64_t)b * p.kv_stride;
-    if constexpr (RATIO == 1) {
-      j.k0 = j.s0 = j.s1 = nullptr;
-      j.c = pos;
-      j.rot_pos = pos;
-      compress_row<L, RATIO, MODE>(p, kv, w, j);
-    } else {
-      j.s1 = p.score + (int64_t)b * p.score_stride;
-      if (pos & 1) {
-        j.k0 = p.state + (int64_t)b * 2 * kDim;
-        j.s0 = j.k0 + kDim;
-        j.c = pos >> 1;
-        j.rot_pos = pos - 1;
-        compress_row<L, RATIO, MODE>(p, kv, w, j);
-      } else {
-        write_state(p, b, b);
-      }
-    }
+    const int32_t b = lo;
+    const int64_t lat0 = uniform(row_start[b]);
+    run_tile<L, RATIO, kTileRows>(p, kv, w, b, item - uniform(item_start[b]), lat0,
+                                  uniform(row_start[b + 1]) - lat0, ld_ro(p.offsets + b),
+                                  ld_ro(p.offsets + S + b), ld_ro(p.start_pos + b));
   }
 }
 
-template <int L, int RATIO, int MODE>
-hipError_t launch_one(const CompressParams& p, hipStream_t stream) {
-  int blocks;
-  size_t lds = 0;
-  if (MODE == 0) {
-    const int64_t items_hint = p.max_out_rows + p.num_slots;
-    int64_t b = (items_hint + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int cap = launch_tuning().compress_blocks > 0 ? launch_tuning().compress_blocks : 4096;
-    if (b > cap) b = cap;
-    blocks = (int)(b < 1 ? 1 : b);
-    lds = sizeof(int32_t) * 2 * (size_t)(p.num_slots + 1);
-  } else {
-    blocks = (p.num_slots + kWavesPerBlock - 1) / kWavesPerBlock;
+template <int L, int RATIO>
+__global__ __launch_bounds__(kBlock) void compress_decode_kernel(CompressParams p) {
+  const PagedKV<L> kv{p.cache.base, p.cache.page_stride, p.cache.num_pages, p.cache.page_bits};
+  const int lane = lane_id();
+  const int64_t b64 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  if (b64 >= p.num_slots) return;
+  const int32_t b = (int32_t)b64;
+  const int64_t pos = ld_ro(p.start_pos + b);
+  if (pos < 0) return;
+  if (RATIO == 2 && (pos & 1) == 0) {          // first token of a pair: keep it pending
+    write_state(p, b, b);
+    return;
   }
-  hipLaunchKernelGGL((compress_kernel<L, RATIO, MODE>), dim3(blocks), dim3(kBlock), lds, stream, p);
+  const uint4 wr = ld_u4(p.norm_w + kDimsPerLane * lane);
+  const float w[8] = {bf16_lo(wr.x), bf16_hi(wr.x), bf16_lo(wr.y), bf16_hi(wr.y),
+                      bf16_lo(wr.z), bf16_hi(wr.z), bf16_lo(wr.w), bf16_hi(wr.w)};
+  RowJob j;
+  j.slot = b;
+  j.latent_idx = b;
+  j.t1 = b;
+  j.from_state = RATIO == 2;
+  j.rot_pos = RATIO == 2 ? pos - 1 : pos;
+  const int64_t c = RATIO == 2 ? (pos >> 1) : pos;
+  // destination: the caller's out_loc (0 = padded row) or the page table
+  if (p.out_loc != nullptr) {
+    j.loc = ld_ro(p.out_loc + b);
+    j.loc_err = 0;
+  } else {
+    page_loc(p, b, c, j.loc, j.loc_err);
+  }
+  finish_row<L, RATIO>(p, kv, w, j, load_row<RATIO>(p, j));
+}
+
+template <int L, int RATIO>
+hipError_t launch_one(const CompressParams& p, hipStream_t stream) {
+  if (p.mode == 0) {
+    // an upper bound on the work items: full tiles of the latent capacity plus
+    // up to two partial tiles (or one tail item) per slot
+    const int64_t items_hint = (p.max_out_rows >> p.tile_log2) + 2 * (int64_t)p.num_slots + 1;
+    int64_t blocks = (items_hint + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int cap = launch_tuning().compress_blocks > 0 ? launch_tuning().compress_blocks : 1024;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    const size_t lds = sizeof(int32_t) * 2 * (size_t)(p.num_slots + 1);
+    const bool small = p.num_slots <= kLanes;
+#define KVC_PREFILL_LAUNCH(R)                                                                     \
+  if (small)                                                                                      \
+    hipLaunchKernelGGL((compress_prefill_small_kernel<L, RATIO, R>), dim3((int)blocks),           \
+                       dim3(kBlock), 0, stream, p);                                               \
+  else                                                                                            \
+    hipLaunchKernelGGL((compress_prefill_kernel<L, RATIO, R>), dim3((int)blocks), dim3(kBlock),  \
+                       lds, stream, p);
+    switch (p.tile_log2) {
+      case 0: KVC_PREFILL_LAUNCH(1) break;
+      case 1: KVC_PREFILL_LAUNCH(2) break;
+      default: KVC_PREFILL_LAUNCH(4) break;
+    }
+#undef KVC_PREFILL_LAUNCH
+  } else {
+    const int blocks = (p.num_slots + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL((compress_decode_kernel<L, RATIO>), dim3(blocks), dim3(kBlock), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
 template <int L>
 hipError_t launch_layout(const CompressParams& p, hipStream_t stream) {
-  if (p.ratio == 1) {
-    return p.mode == 0 ? launch_one<L, 1, 0>(p, stream) : launch_one<L, 1, 1>(p, stream);
-  }
-  return p.mode == 0 ? launch_one<L, 2, 0>(p, stream) : launch_one<L, 2, 1>(p, stream);
+  return p.ratio == 1 ? launch_one<L, 1>(p, stream) : launch_one<L, 2>(p, stream);
 }
 
 }  // namespace
 
 int max_prefill_slots() { return kMaxPrefillSlots; }
 
-hipError_t launch_compress(const CompressParams& p, hipStream_t stream) {
+hipError_t launch_compress(const CompressParams& p_in, hipStream_t stream) {
+  CompressParams p = p_in;
+  // rows per work item: 1, 2 or 4, no more than a page
+  int tl = launch_tuning().compress_tile_log2 >= 0 ? launch_tuning().compress_tile_log2 : kTileLog2;
+  tl = tl > 2 ? 2 : tl;
+  p.tile_log2 = tl < p.cache.page_bits ? tl : p.cache.page_bits;
   switch (p.cache.layout) {
     case kV41: return launch_layout<kV41>(p, stream);
     case kV41Fp4: return launch_layout<kV41Fp4>(p, stream);

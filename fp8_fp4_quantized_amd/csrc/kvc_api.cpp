@@ -109,11 +109,20 @@ int kvc_layout_query(int32_t layout, kvc_layout_info* info) {
   return ok();
 }
 
-int kvc_set_launch_shape(int32_t gather_blocks, int32_t compress_blocks) {
-  if (gather_blocks < 0 || compress_blocks < 0)
-    return fail(KVC_EINVAL, "kvc_set_launch_shape: negative block count");
+int kvc_set_launch_shape(int32_t gather_blocks, int32_t compress_blocks,
+                         int32_t compress_tile_rows) {
+  if (gather_blocks < 0 || compress_blocks < 0 || compress_tile_rows < 0 ||
+      compress_tile_rows > 4 || (compress_tile_rows & (compress_tile_rows - 1)) != 0)
+    return fail(KVC_EINVAL, "kvc_set_launch_shape: negative block count, or tile rows not 1, 2 "
+                            "or 4");
   kvc::launch_tuning().gather_blocks = gather_blocks;
   kvc::launch_tuning().compress_blocks = compress_blocks;
+  int tl = -1;
+  if (compress_tile_rows > 0) {
+    tl = 0;
+    while ((1 << tl) < compress_tile_rows) ++tl;
+  }
+  kvc::launch_tuning().compress_tile_log2 = tl;
   return ok();
 }
 

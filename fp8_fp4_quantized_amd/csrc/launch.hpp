@@ -60,6 +60,7 @@ struct CompressParams {
   uint16_t* prequant;
   int64_t prequant_stride;
   int32_t* status;
+  int32_t tile_log2;           // set by the launcher: log2 of rows per prefill work item
 };
 
 // Each launcher enqueues one kernel on `stream` and returns the HIP error of
@@ -75,6 +76,7 @@ int max_prefill_slots();
 struct LaunchTuning {
   int gather_blocks;           // workgroups of the gather grid
   int compress_blocks;         // workgroups of the prefill compress grid
+  int compress_tile_log2;      // log2 of compressed rows per prefill work item (-1: default)
 };
 LaunchTuning& launch_tuning();
 

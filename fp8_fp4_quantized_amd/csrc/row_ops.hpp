@@ -72,11 +72,12 @@ __device__ __forceinline__ void store_row_wave<kV41>(uint4 x, uint8_t* data, uin
   for (int k = 0; k < 8; ++k) c[k] = fp8_from_bf16(h[k], E);
   const uint32_t w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
   const uint32_t w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-  uint32_t sc[4];
-  collect_scale_bytes<4, 4>((uint32_t)E, sc);
+  // scale bytes: group g's E sits on lanes 4g..4g+3; lane 16k+12 packs the
+  // bytes of groups 4k..4k+3 and the four packing lanes store 16 B
+  const uint32_t sw = pack4_bytes_shr<4>((uint32_t)E);
   if (!write) return;
   *(u32x2*)(data + 8 * lane) = u32x2{w0, w1};
-  if (lane == 0) st_u4(scale, make_uint4(sc[0], sc[1], sc[2], sc[3]));
+  if ((lane & 15) == 12) *(uint32_t*)(scale + 4 * (lane >> 4)) = sw;
 }
 
 template <>
@@ -113,73 +114,41 @@ __device__ __forceinline__ void store_row_wave<kV41Fp4>(uint4 x, uint8_t* data, 
   const float q = __fdiv_rn(__uint_as_float(amax << 16), 6.0f);
   const uint32_t sc = e4m3_satfinite(q);
   const float s = e4m3_to_f32(sc);
-  const Fp4Thresholds t = fp4_thresholds(s);
-  const uint32_t h[8] = {x.x & 0xFFFFu, x.x >> 16, x.y & 0xFFFFu, x.y >> 16,
-                         x.z & 0xFFFFu, x.z >> 16, x.w & 0xFFFFu, x.w >> 16};
+  const float rs = __builtin_amdgcn_rcpf(s);
+  const float xf[8] = {bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y),
+                       bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
   uint32_t w = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) w |= fp4_from_bf16(h[k], t) << (4 * k);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fp4_quotient(xf[0], rs), fp4_quotient(xf[1], rs), 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fp4_quotient(xf[2], rs), fp4_quotient(xf[3], rs), 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fp4_quotient(xf[4], rs), fp4_quotient(xf[5], rs), 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fp4_quotient(xf[6], rs), fp4_quotient(xf[7], rs), 1.0f, 3);
   w = sc == 0 ? 0u : w;                            // zero scale: all codes 0
-  uint32_t sb[8];
-  collect_scale_bytes<8, 2>(sc, sb);
+  // scale bytes: group g's code sits on lanes 2g, 2g+1; lane 8k+6 packs the
+  // bytes of groups 4k..4k+3 and the eight packing lanes store 32 B
+  const uint32_t sw = pack4_bytes_shr<2>(sc);
   if (!write) return;
   *(uint32_t*)(data + 4 * lane) = w;
-  if (lane == 0) {
-    st_u4(scale, make_uint4(sb[0], sb[1], sb[2], sb[3]));
-    st_u4(scale + 16, make_uint4(sb[4], sb[5], sb[6], sb[7]));
-  }
+  if ((lane & 7) == 6) *(uint32_t*)(scale + 4 * (lane >> 3)) = sw;
 }
 
 // ------------------------------------------------------------------ dequant
-// fp8 e4m3fn codes (4 per word) times 2^(E - 127) -> 4 bf16 (two words).
-// Fast path: for 3 <= E <= 254 the product is exact in bf16 or overflows to
-// infinity in fp32, so the top half of the fp32 product is the answer.  The
-// fp32 built from the code's low 7 bits placed at bit 20 equals the code's
-// value times 2^-120 for normal and subnormal codes alike (fp32 denormals
-// are kept on gfx950), and ldexp adds E - 7.
-__device__ __forceinline__ float fp8_scaled(uint32_t c, int E) {
-  const float f = __uint_as_float(((c & 0x80u) << 24) | ((c & 0x7Fu) << 20));
-  return __builtin_amdgcn_ldexpf(f, E - 7);
-}
 __device__ __forceinline__ uint32_t bf16_top(float f) { return __float_as_uint(f) >> 16; }
 
-__device__ __forceinline__ uint2 dq_fp8x4_fast(uint32_t w, int E) {
-  const uint32_t b0 = bf16_top(fp8_scaled(w & 0xFFu, E));
-  const uint32_t b1 = bf16_top(fp8_scaled((w >> 8) & 0xFFu, E));
-  const uint32_t b2 = bf16_top(fp8_scaled((w >> 16) & 0xFFu, E));
-  const uint32_t b3 = bf16_top(fp8_scaled(w >> 24, E));
-  return make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-}
-
-// general path: any E (255 = NaN scale), NaN codes, and rounding of the
-// products that fall below the bf16 subnormal grid (E <= 2)
-__device__ __forceinline__ uint32_t dq_fp8_general(uint32_t c, int E) {
-  if (E == 255 || (c & 0x7Fu) == 0x7Fu) return 0x7FC0u;
-  uint32_t u = __float_as_uint(fp8_scaled(c, E));
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-__device__ __forceinline__ uint2 dq_fp8x4_general(uint32_t w, int E) {
-  return make_uint2(dq_fp8_general(w & 0xFFu, E) | (dq_fp8_general((w >> 8) & 0xFFu, E) << 16),
-                    dq_fp8_general((w >> 16) & 0xFFu, E) | (dq_fp8_general(w >> 24, E) << 16));
-}
-
-// any byte of w equal to 0x7F or 0xFF (an e4m3fn NaN)
-__device__ __forceinline__ bool has_nan_fp8(uint32_t w) {
-  return (((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) != 0u;
-}
-
-// 8 fp8 codes + their ue8m0 exponent -> 8 bf16
-__device__ __forceinline__ uint4 dq_fp8x8(uint2 codes, int E) {
-  uint2 lo, hi;
-  if ((unsigned)(E - 3) <= 251u && !has_nan_fp8(codes.x) && !has_nan_fp8(codes.y)) {
-    lo = dq_fp8x4_fast(codes.x, E);
-    hi = dq_fp8x4_fast(codes.y, E);
-  } else {
-    lo = dq_fp8x4_general(codes.x, E);
-    hi = dq_fp8x4_general(codes.y, E);
-  }
-  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+// 8 fp8 codes + their ue8m0 exponent E -> 8 bf16.  gfx950's scaled
+// conversion v_cvt_scalef32_pk_bf16_fp8 multiplies two e4m3fn codes by the
+// power of two whose biased exponent is the fp32 scale's exponent field -- E
+// itself here -- so it computes fp8 * 2^(E - 127) rounded to bf16, with NaN
+// for NaN codes and for E = 255.  The products are exact in bf16 for E >= 3;
+// the device tests compare it with the oracle for every code under every E.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 dq_fp8x8(uint2 codes, uint32_t E) {
+  const float sc = __uint_as_float(E << 23);
+  const bf16x2_hw a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, sc, false);
+  const bf16x2_hw b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, sc, true);
+  const bf16x2_hw c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, sc, false);
+  const bf16x2_hw d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, sc, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
 }
 
 // 8 e2m1 codes (nibbles, dim order from the low nibble) + their e4m3 scale

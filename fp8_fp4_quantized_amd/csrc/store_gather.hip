@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kBlock) void store_rows_kernel(StoreParams p) {
 
 // ------------------------------------------------------------------ gather
 // rows handled together by one wave per loop trip
-constexpr int kGatherUnroll = 4;
+constexpr int kGatherUnroll = 8;
 
 template <int L> struct LaneCodes;          // this lane's share of a row
 template <> struct LaneCodes<kV41> { uint2 codes; uint32_t scale; };
@@ -94,7 +94,7 @@ template <int L>
 __device__ __forceinline__ uint4 decode_lane(const LaneCodes<L>& c, int lane);
 template <>
 __device__ __forceinline__ uint4 decode_lane<kV41>(const LaneCodes<kV41>& c, int) {
-  return dq_fp8x8(c.codes, (int)c.scale);
+  return dq_fp8x8(c.codes, c.scale);
 }
 template <>
 __device__ __forceinline__ uint4 decode_lane<kV41Fp4>(const LaneCodes<kV41Fp4>& c, int) {
@@ -103,57 +103,67 @@ __device__ __forceinline__ uint4 decode_lane<kV41Fp4>(const LaneCodes<kV41Fp4>& 
 template <>
 __device__ __forceinline__ uint4 decode_lane<kV4>(const LaneCodes<kV4>& c, int lane) {
   if (lane >= kRopeLane0) return c.raw;
-  return dq_fp8x8(make_uint2(c.raw.x, c.raw.y), (int)c.scale);
+  return dq_fp8x8(make_uint2(c.raw.x, c.raw.y), c.scale);
 }
 
+// A wave takes the rows of the gather 64 at a time: lane i reads id i of the
+// batch and resolves it to a physical slot (one vector load of ids, one of
+// page-table entries), then the rows are expanded kGatherUnroll at a time,
+// their slots broadcast with v_readlane, all their loads issued before any
+// store.
 template <int L>
 __global__ __launch_bounds__(kBlock) void dequant_gather_kernel(GatherParams p) {
   const PagedKV<L> kv = paged<L>(p.cache);
   const int lane = lane_id();
   const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  const int64_t page_mask = (int64_t(1) << p.cache.page_bits) - 1;
+  const int32_t page_mask = (1 << p.cache.page_bits) - 1;
 
-  for (int64_t base = wave0 * kGatherUnroll; base < p.n; base += nwaves * kGatherUnroll) {
-    int64_t slot[kGatherUnroll];
-    bool live[kGatherUnroll];
-#pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) {
-      const int64_t r = base + u;
-      const int64_t id = r < p.n ? (int64_t)uniform(p.ids[r]) : -1;
-      int64_t s = -1;
+  for (int64_t b0 = wave0 * kLanes; b0 < p.n; b0 += nwaves * kLanes) {
+    // ---- resolve this lane's id to a slot (-1: zero row)
+    const int64_t r = b0 + lane;
+    int32_t slot = -1;
+    int32_t bad = 0;
+    if (r < p.n) {
+      const int32_t id = p.ids[r];
       if (id >= 0) {
         if (p.page_table != nullptr) {
-          const int64_t lp = id >> p.cache.page_bits;
+          const int32_t lp = id >> p.cache.page_bits;
           if (lp < p.n_pages) {
-            const int64_t phys = uniform(p.page_table[lp]);
+            const int32_t phys = p.page_table[lp];
             if (phys >= 0 && phys < kv.num_pages) {
-              s = (phys << p.cache.page_bits) | (id & page_mask);
+              slot = (phys << p.cache.page_bits) | (id & page_mask);
             } else {
-              raise_status(p.status, kStPageRange);
+              bad = kStPageRange;
             }
           } else {
-            raise_status(p.status, kStIdRange);
+            bad = kStIdRange;
           }
         } else if (kv.valid(id)) {
-          s = id;
+          slot = id;
         } else {
-          raise_status(p.status, kStIdRange);
+          bad = kStIdRange;
         }
       }
-      slot[u] = s;
-      live[u] = s >= 0;
     }
-    LaneCodes<L> c[kGatherUnroll];
+    if (bad != 0 && p.status != nullptr) atomicOr(p.status, bad);
+
+    // ---- expand the batch's rows
+    const int cnt = (int)(p.n - b0 < kLanes ? p.n - b0 : kLanes);
+    for (int j = 0; j < cnt; j += kGatherUnroll) {
+      int32_t s[kGatherUnroll];
+      LaneCodes<L> c[kGatherUnroll];
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u)
-      if (live[u]) c[u] = load_lane<L>(kv, slot[u], lane);
+      for (int u = 0; u < kGatherUnroll; ++u) {
+        s[u] = j + u < cnt ? __builtin_amdgcn_readlane(slot, j + u) : -1;
+        if (s[u] >= 0) c[u] = load_lane<L>(kv, s[u], lane);
+      }
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) {
-      const int64_t r = base + u;
-      if (r >= p.n) break;
-      const uint4 o = live[u] ? decode_lane<L>(c[u], lane) : make_uint4(0u, 0u, 0u, 0u);
-      st_u4_nt(p.out + r * p.out_stride + kDimsPerLane * lane, o);
+      for (int u = 0; u < kGatherUnroll; ++u) {
+        if (j + u >= cnt) break;
+        const uint4 o = s[u] >= 0 ? decode_lane<L>(c[u], lane) : make_uint4(0u, 0u, 0u, 0u);
+        st_u4_nt(p.out + (b0 + j + u) * p.out_stride + kDimsPerLane * lane, o);
+      }
     }
   }
 }
@@ -173,7 +183,7 @@ int grid_for(int64_t units, int64_t per_block, int cap) {
 }  // namespace
 
 LaunchTuning& launch_tuning() {
-  static LaunchTuning t{0, 0};
+  static LaunchTuning t{0, 0, -1};
   return t;
 }
 
@@ -187,7 +197,7 @@ hipError_t launch_store_rows(const StoreParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_dequant_gather(const GatherParams& p, hipStream_t stream) {
-  int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * kGatherUnroll, 4096);
+  int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * kLanes, 2048);
   if (launch_tuning().gather_blocks > 0) blocks = launch_tuning().gather_blocks;
   switch (p.cache.layout) {
     case kV41: return launch(dequant_gather_kernel<kV41>, blocks, p, stream);

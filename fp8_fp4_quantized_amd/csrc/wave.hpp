@@ -2,7 +2,7 @@
 //
 // Group reductions over 2, 4, 8 or 16 neighbouring lanes use DPP (quad
 // permutes, then the half-row and row mirrors), which never leave the VALU;
-// the last two steps of a whole-wave sum go through ds_swizzle/bpermute.
+// a whole-wave sum finishes with the gfx9 row broadcasts and a readlane.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,6 +15,8 @@ constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7-i within each 8
 constexpr int kDppRowMirror = 0x140;      // lane i <-> 15-i within each 16
+constexpr int kDppRowBcast15 = 0x142;     // lane 15 of each row into the next row
+constexpr int kDppRowBcast31 = 0x143;     // lane 31 into rows 2 and 3
 
 template <int Ctrl>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
@@ -37,18 +39,42 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
   return v;
 }
 
-// sum over the whole wave; every lane receives the total
+// sum over the whole wave, returned as a wave-uniform value: each 16-lane row
+// is reduced with DPP, row_bcast:15 / row_bcast:31 fold the rows into lane
+// 63, and v_readlane broadcasts it (no LDS traffic)
 __device__ __forceinline__ float wave_sum_f32(float v) {
   v += dpp_f32<kDppQuadXor1>(v);
   v += dpp_f32<kDppQuadXor2>(v);
   v += dpp_f32<kDppRowHalfMirror>(v);
   v += dpp_f32<kDppRowMirror>(v);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast15, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast31, 0xC, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Pack one byte from each of four lanes spaced D apart into a dword on the
+// last of them: lane l receives byte(v[l-3D]) | byte(v[l-2D]) << 8 |
+// byte(v[l-D]) << 16 | byte(v[l]) << 24.  The lanes read must lie in l's
+// 16-lane row (DPP row_shr), which the callers' lane choice guarantees.
+template <int D>
+__device__ __forceinline__ uint32_t pack4_bytes_shr(uint32_t v) {
+  const uint32_t b0 = dpp_u32<0x110 + 3 * D>(v) & 0xFFu;   // row_shr:3D
+  const uint32_t b1 = dpp_u32<0x110 + 2 * D>(v) & 0xFFu;   // row_shr:2D
+  const uint32_t b2 = dpp_u32<0x110 + D>(v) & 0xFFu;       // row_shr:D
+  return b0 | (b1 << 8) | (b2 << 16) | ((v & 0xFFu) << 24);
 }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// Load from memory that no thread writes while the kernel runs (the caller's
+// read-only inputs: offsets, positions, page tables, ids).  Going through the
+// constant address space lets the compiler use a scalar load when the address
+// is wave-uniform; its completion is then tracked by lgkmcnt, so waiting for
+// it never waits for outstanding vector stores.
+template <typename T>
+__device__ __forceinline__ T ld_ro(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
 
 // a value the compiler may keep in a scalar register (the caller guarantees
 // it is the same on every active lane)

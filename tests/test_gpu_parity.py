@@ -317,6 +317,22 @@ def test_compress_prefill_ragged(K, layout, ratio):
     _check_compress(r, layout, 16, slots, lat)
 
 
+@pytest.mark.parametrize("layout,ratio", [("V41_FP4", 2), ("V41", 1), ("V4", 2)])
+def test_compress_prefill_many_slots(K, layout, ratio):
+    """more slots than a wave has lanes (the LDS-table path): 150 slots with
+    lengths 0..40 and random (odd and even) start positions."""
+    _say("compress many slots", layout, ratio)
+    rng = np.random.default_rng(123 + ratio)
+    lengths = rng.integers(0, 41, size=150)
+    P = rng.integers(0, 200, size=150)
+    case = W.compress_case(90 + ratio, lengths, start_pos=P, ratio=ratio, page_size=8,
+                           fused=True, gap=1)
+    r = _run_compress(K, case, layout, ratio, oracle.PREFILL)
+    lat, slots = _prefill_slots(case, ratio)
+    assert r["n_rows"] == len(lat)
+    _check_compress(r, layout, 8, slots, lat)
+
+
 def test_compress_c1(K):
     """one request of 64 tokens, ratio 2, separate kv / score buffers, V41,
     page 64 -> 32 rows; then a gather of the 32 rows."""
