@@ -28,35 +28,26 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["fp8_fp4_quantized_amd/csrc/store_gather.hip",
-                  "fp8_fp4_quantized_amd/csrc/row_ops.hpp",
-                  "fp8_fp4_quantized_amd/csrc/codec.hpp",
-                  "fp8_fp4_quantized_amd/csrc/layout.hpp",
-                  "fp8_fp4_quantized_amd/csrc/wave.hpp"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or
-    None when the kernel sources changed since they were taken."""
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    runs (profiles/traffic.json), or None when the kernel's sources changed
+    since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as fh:
-            t = json.load(fh)
-    except (OSError, ValueError):
+            e = json.load(fh).get(kernel)
+        h = hashlib.sha256()
+        for f in e["source_files"]:
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+    except (OSError, ValueError, KeyError, TypeError, AttributeError):
         return None
-    e = t.get(kernel)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if h.hexdigest()[:16] != e.get("source_hash"):
         return None
     return e.get("bytes_per_launch")
 
@@ -64,12 +55,15 @@ def measured_traffic(kernel: str):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gather-blocks", type=int, default=0)
     ap.add_argument("--compress-blocks", type=int, default=0)
     ap.add_argument("--compress-tile-rows", type=int, default=0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device-to-device copy 5 times (the known-size "
+                         "reference for the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path runs on one GPU's share); "
@@ -84,6 +78,15 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                          "launches": 5}), flush=True)
+        return 0
     kvc.kvc_set_launch_shape(args.gather_blocks, args.compress_blocks, args.compress_tile_rows)
 
     def d(a):
@@ -183,7 +186,8 @@ def main() -> int:
         "kernels": {
             "compress_store": {"us": float(np.mean(comp_ms)) * 1e3, "p90_us": float(np.percentile(comp_ms, 90)) * 1e3,
                                "bytes": comp_bytes, "gbps": comp_gbs, "frac": comp_gbs / HBM_PEAK_GBS,
-                               "rows_per_s": c3_rows / comp_s},
+                               "rows_per_s": c3_rows / comp_s,
+                               "traffic": measured_traffic("compress_store")},
             "dequant_gather": {"us": float(np.mean(gath_ms)) * 1e3, "p90_us": float(np.percentile(gath_ms, 90)) * 1e3,
                                "bytes": gath_bytes, "gbps": gath_gbs, "frac": gath_gbs / HBM_PEAK_GBS,
                                "rows_per_s": n_ids / gath_s},
