@@ -20,8 +20,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "libkvc_oracle.so")
 
 LAYOUTS = {"V4": 0, "V41": 1, "V41_FP4": 2}
-PREFILL, DECODE = 0, 1
+PREFILL, DECODE, VERIFY = 0, 1, 2
 ST_ID_RANGE, ST_PAGE_RANGE, ST_PT_RANGE, ST_LATENT_RANGE, ST_POS_RANGE = 1, 2, 4, 8, 16
+ST_REQ_RANGE = 32
 
 _lib = None
 
@@ -45,6 +46,8 @@ class _CompressArgs(C.Structure):
         ("latent", C.c_void_p), ("latent_stride", C.c_int64), ("max_out_rows", C.c_int64),
         ("prequant", C.c_void_p), ("prequant_stride", C.c_int64),
         ("cache", _Cache), ("status", C.c_void_p),
+        ("draft_len", C.c_int32), ("ring_slots", C.c_int32),
+        ("dcp_world", C.c_int32), ("dcp_rank", C.c_int32), ("dcp_interleave", C.c_int32),
     ]
 
 
@@ -78,6 +81,10 @@ def lib():
             "kvo_compress": (None, [C.POINTER(_CompressArgs)]),
             "kvo_count_rows": (i64, [C.POINTER(_CompressArgs)]),
             "kvo_num_threads": (C.c_int, []),
+            "kvo_store_rows_rope": (None, [C.POINTER(_Cache), vp, i64, vp, vp, i64, vp, i64, vp, vp]),
+            "kvo_dcp_owner": (i32, [i64, i32, i32, C.POINTER(C.c_int64)]),
+            "kvo_dcp_filter_ids": (None, [vp, i64, i32, i64, vp, i32, vp, i64, vp, i32, i64,
+                                          i32, i32, i32, vp, i64, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -210,6 +217,48 @@ def store_rows(cache: np.ndarray, layout: str, page_size: int, rows, out_loc) ->
     return int(st[0])
 
 
+def store_rows_rope(cache: np.ndarray, layout: str, page_size: int, rows, positions, freqs,
+                    out_loc):
+    """Rotate the rope dims of bf16 ``rows [n, 512]`` at ``positions`` and
+    quantize them into ``cache`` (in place).  -> (rotated rows ``[n, 512]``,
+    zero for rows not stored; status)."""
+    rows = _c(rows, np.uint16).reshape(-1, 512)
+    positions = _c(positions, np.int32)
+    out_loc = _c(out_loc, np.int32)
+    freqs = _c(freqs, np.float32)
+    rot = np.zeros_like(rows)
+    st = np.zeros(1, np.int32)
+    cd = _cache(cache, layout, page_size)
+    lib().kvo_store_rows_rope(C.byref(cd), _p(rows), 512, _p(positions), _p(freqs),
+                              freqs.shape[0], _p(out_loc), rows.shape[0], _p(rot), _p(st))
+    return rot, int(st[0])
+
+
+def dcp_owner(c: int, world: int, interleave: int) -> tuple[int, int]:
+    """(owner rank, ordinal among the owner's rows) of compressed row ``c``."""
+    local = C.c_int64(0)
+    r = lib().kvo_dcp_owner(int(c), int(world), int(interleave), C.byref(local))
+    return int(r), int(local.value)
+
+
+def dcp_filter_ids(ids, token_to_req, block_table, *, page_size, num_pages, world, rank,
+                   interleave, valid=None):
+    """One rank's share of global ids ``[T, k]`` -> (slots ``[T, k]`` with a
+    -1 tail, lens ``[T]``, status)."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    t2r = _c(token_to_req, np.int32)
+    bt = _c(block_table, np.int32)
+    va = None if valid is None else _c(valid, np.int32)
+    slots = np.zeros((T, k), np.int32)
+    lens = np.zeros(T, np.int32)
+    st = np.zeros(1, np.int32)
+    lib().kvo_dcp_filter_ids(_p(ids), T, k, k, _p(t2r), bt.shape[0], _p(bt), bt.shape[1],
+                             _p(va), page_size, num_pages, world, rank, interleave,
+                             _p(slots), k, _p(lens), _p(st))
+    return slots, lens, int(st[0])
+
+
 def dequant_gather(cache: np.ndarray, layout: str, page_size: int, page_table, ids):
     """-> (bf16 rows ``[n, 512]``, status)."""
     ids = _c(ids, np.int32)
@@ -225,13 +274,15 @@ def dequant_gather(cache: np.ndarray, layout: str, page_size: int, page_table, i
 # ---------------------------------------------------------------- compressor
 def compress(*, ratio, mode, kv, score=None, fused=False, offsets=None, start_pos,
              page_table=None, out_loc=None, state, norm_w, eps, freqs, cache,
-             layout, page_size, max_out_rows=None, want_prequant=True):
+             layout, page_size, max_out_rows=None, want_prequant=True, draft_len=1,
+             ring_slots=1, dcp_world=1, dcp_rank=0, dcp_interleave=1):
     """Run the compressor.  ``kv`` is ``[T, 512]`` (or ``[T, 1024]`` with
     ``fused=True``: kv in columns 0..511, score in 512..1023).  ``state`` and
     ``cache`` are updated in place.  Returns (latent, prequant, status,
     n_rows); latent / prequant have ``max_out_rows`` rows (default: the
-    number of rows the plan emits in prefill, the slot count in decode) and
-    untouched rows stay zero."""
+    number of rows the plan emits in prefill, the token count in decode and
+    verify) and untouched rows stay zero.  ``state`` is ``[S, ring_slots, 2,
+    512]`` (``[S, 2, 512]`` for one entry)."""
     kv = _c(kv, np.uint16)
     S = int(np.asarray(start_pos).size)
     if fused:
@@ -265,9 +316,11 @@ def compress(*, ratio, mode, kv, score=None, fused=False, offsets=None, start_po
     a.freqs, a.max_pos = _p(freqs), freqs.shape[0]
     a.cache = _cache(cache, layout, page_size)
     a.status = _p(st)
+    a.draft_len, a.ring_slots = draft_len, ring_slots
+    a.dcp_world, a.dcp_rank, a.dcp_interleave = dcp_world, dcp_rank, dcp_interleave
     n_rows = lib().kvo_count_rows(C.byref(a))
     if max_out_rows is None:
-        max_out_rows = n_rows if mode == PREFILL else S
+        max_out_rows = n_rows if mode == PREFILL else S * (draft_len if mode == VERIFY else 1)
     latent = np.zeros((max(max_out_rows, 1), 512), np.uint16)
     pre = np.zeros_like(latent) if want_prequant else None
     a.latent, a.latent_stride, a.max_out_rows = latent.ctypes.data, 512, max_out_rows

@@ -328,6 +328,48 @@ void kvo_store_rows(const kvo_cache* c, const uint16_t* rows, int64_t row_stride
   }
 }
 
+/* Store with an in-kernel rotary embedding [PR39652-S: the cache writer
+ * with optional RoPE for the V4.1 layouts]: row i's dims (448+2j, 449+2j)
+ * are rotated by (cos, sin) = (freqs[positions[i]][2j], freqs[positions[i]][2j+1])
+ * in fp64 and rounded once to bf16, the other dims pass unchanged, and the
+ * result is stored as kvo_store_rows stores (any layout).  Readings: the
+ * rotation is the one the compressors apply (interleaved pairs of the last
+ * 64 dims); a padded row (out_loc 0) is skipped before its position is
+ * looked at; a position outside the table skips the row with
+ * KVO_ST_POS_RANGE.  `rotated` (NULL or n x 512) receives the rotated bf16
+ * rows of the rows that are stored. */
+void kvo_store_rows_rope(const kvo_cache* c, const uint16_t* rows, int64_t row_stride,
+                         const int32_t* positions, const float* freqs, int64_t max_pos,
+                         const int32_t* out_loc, int64_t n, uint16_t* rotated,
+                         int32_t* status) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    int32_t loc = out_loc[i];
+    if (loc == 0) continue;
+    int64_t p = positions[i];
+    if (p < 0 || p >= max_pos) {
+      set_status(status, KVO_ST_POS_RANGE);
+      continue;
+    }
+    if (loc < 0 || loc / c->page_size >= c->num_pages) {
+      set_status(status, KVO_ST_PAGE_RANGE);
+      continue;
+    }
+    const uint16_t* x = rows + i * row_stride;
+    uint16_t z[KVO_D];
+    memcpy(z, x, sizeof z);
+    const float* f = freqs + p * KVO_ROPE;
+    for (int j = 0; j < KVO_ROPE / 2; ++j) {
+      double xr = kvo_bf16_decode(x[KVO_NOPE + 2 * j]), xi = kvo_bf16_decode(x[KVO_NOPE + 2 * j + 1]);
+      double cs = f[2 * j], sn = f[2 * j + 1];
+      z[KVO_NOPE + 2 * j] = kvo_bf16_encode(xr * cs - xi * sn);
+      z[KVO_NOPE + 2 * j + 1] = kvo_bf16_encode(xr * sn + xi * cs);
+    }
+    if (rotated) memcpy(rotated + i * KVO_D, z, sizeof z);
+    kvo_store_row(c->layout, z, row_data(c, loc), row_scale(c, loc));
+  }
+}
+
 /* Gather rows by id and expand them to bf16.  With a page table the ids are
  * logical rows mapped through it [FI-topk]; without one they are physical
  * slots.  A negative id yields a zero row (reading: the -1 padding of top-k
@@ -385,6 +427,7 @@ typedef struct {
   const uint16_t* k1;    /* second (or only) token */
   const uint16_t* s1;
   int64_t latent_idx;
+  int64_t token;         /* decode / verify: the token's index into out_loc */
 } kvo_row;
 
 static void pool_norm_rope(const kvo_compress_args* a, const kvo_row* r,
@@ -416,18 +459,43 @@ static void pool_norm_rope(const kvo_compress_args* a, const kvo_row* r,
   for (int d = 0; d < KVO_D; ++d) z_out[d] = kvo_bf16_encode(z[d]);
 }
 
+/* ------------------------------------------------------------------------
+ * Decode context parallelism [FI-dcp].  The compressed rows of a request
+ * are dealt to the `world` ranks in runs of `interleave` consecutive rows,
+ * round robin: run u = c / interleave goes to rank u % world.  Each rank
+ * numbers the rows it owns consecutively (its ordinal `local`), and its
+ * pages hold page_size of its own rows, so page-table entry local /
+ * page_size and row local % page_size place row c on its owner.  This is the
+ * pages' de-interleave (virtual block of page_size * world states, owner from
+ * the offset in it) whenever page_size is a multiple of the interleave.
+ * ---------------------------------------------------------------------- */
+int32_t kvo_dcp_owner(int64_t c, int32_t world, int32_t interleave, int64_t* local) {
+  if (world <= 1) {
+    if (local) *local = c;
+    return 0;
+  }
+  int64_t u = c / interleave;
+  if (local) *local = (u / world) * interleave + c % interleave;
+  return (int32_t)(u % world);
+}
+
 /* destination slot of a row, or 0 when nothing is written */
 static int64_t row_out_loc(const kvo_compress_args* a, const kvo_row* r) {
   const kvo_cache* c = &a->cache;
   int64_t loc;
-  if (a->mode == KVO_DECODE && a->out_loc) {
-    loc = a->out_loc[r->slot];
+  if (a->mode != KVO_PREFILL && a->out_loc) {
+    loc = a->out_loc[r->token];
   } else {
-    int64_t lp = r->c / c->page_size;
+    int64_t local = r->c;
+    if (a->dcp_world > 1) {
+      /* rows other ranks own are not stored here */
+      if (kvo_dcp_owner(r->c, a->dcp_world, a->dcp_interleave, &local) != a->dcp_rank) return 0;
+    }
+    int64_t lp = local / c->page_size;
     if (lp >= a->pt_stride) { set_status(a->status, KVO_ST_PT_RANGE); return 0; }
     int64_t phys = a->page_table[(int64_t)r->slot * a->pt_stride + lp];
     if (phys < 0 || phys >= c->num_pages) { set_status(a->status, KVO_ST_PAGE_RANGE); return 0; }
-    loc = phys * c->page_size + r->c % c->page_size;
+    loc = phys * c->page_size + local % c->page_size;
   }
   if (loc == 0) return 0;                         /* padded row */
   if (loc < 0 || loc / c->page_size >= c->num_pages) {
@@ -443,15 +511,27 @@ static const uint16_t* tok_kv(const kvo_compress_args* a, int64_t row) {
 static const uint16_t* tok_score(const kvo_compress_args* a, int64_t row) {
   return a->score ? a->score + row * a->score_stride : NULL;
 }
-static uint16_t* state_kv(const kvo_compress_args* a, int32_t b) {
-  return a->state + (int64_t)b * 2 * KVO_D;
+
+/* The pending-state ring of slot b: `ring` entries of (kv, score).  The
+ * first token of pair k (positions 2k, 2k+1) waits in entry k % ring.  One
+ * entry is the single pending token of plain decode [PR39652-R]; more
+ * entries let a verify step that rejects drafts find the pending token an
+ * earlier step left (reading: the multi-slot ring of the verify mode, its
+ * indexing unstated on the pages). */
+static int64_t ring_of(const kvo_compress_args* a) {
+  return a->ring_slots > 1 ? a->ring_slots : 1;
 }
-static uint16_t* state_score(const kvo_compress_args* a, int32_t b) {
-  return a->state + (int64_t)b * 2 * KVO_D + KVO_D;
+static uint16_t* state_kv(const kvo_compress_args* a, int32_t b, int64_t pair) {
+  int64_t e = pair % ring_of(a);
+  return a->state + ((int64_t)b * ring_of(a) + e) * 2 * KVO_D;
+}
+static uint16_t* state_score(const kvo_compress_args* a, int32_t b, int64_t pair) {
+  return state_kv(a, b, pair) + KVO_D;
 }
 
 typedef struct {
-  int32_t slot;
+  uint16_t* kv_dst;
+  uint16_t* score_dst;
   const uint16_t* kv;
   const uint16_t* score;
 } kvo_state_write;
@@ -464,9 +544,14 @@ typedef struct {
  * the slot's pending state when it precedes the extend; a last token at an
  * even position becomes the new pending state (the pair-state ring
  * [PR39652-R]).  Latent rows are numbered consecutively in slot order.
- * Decode: slot b's only token is row b of the buffer at position
- * start_pos[b]; its latent row is b; ratio 2 writes the pending state at
- * even positions and emits the pair's row at odd positions. */
+ * Decode and verify: slot b holds D tokens (D = 1 for decode, draft_len for
+ * verify) at rows b*D..b*D+D-1 with positions start_pos[b]..start_pos[b]+D-1,
+ * taken in order as single decode tokens: ratio 1 emits a row per token;
+ * ratio 2 makes a token at an even position pending and pools a token at an
+ * odd position with the pending one (the previous token of the slot, or the
+ * ring's entry when the pair began before this call).  Token j's latent row
+ * and out_loc entry are b*D + j (reading: the verify batch laid out as D
+ * decode tokens per slot). */
 static int64_t build_plan(const kvo_compress_args* a, kvo_row* rows,
                           kvo_state_write* sw, int64_t* n_sw) {
   int64_t nr = 0, ns = 0;
@@ -479,7 +564,7 @@ static int64_t build_plan(const kvo_compress_args* a, kvo_row* rows,
         for (int64_t t = 0; t < n; ++t) {
           if (rows) {
             kvo_row r = {b, P + t, P + t, NULL, NULL, tok_kv(a, first + t),
-                         tok_score(a, first + t), nr};
+                         tok_score(a, first + t), nr, -1};
             rows[nr] = r;
           }
           ++nr;
@@ -496,46 +581,60 @@ static int64_t build_plan(const kvo_compress_args* a, kvo_row* rows,
               r.k0 = tok_kv(a, first + (q - 1 - P));
               r.s0 = tok_score(a, first + (q - 1 - P));
             } else {
-              r.k0 = state_kv(a, b);
-              r.s0 = state_score(a, b);
+              r.k0 = state_kv(a, b, q / 2);
+              r.s0 = state_score(a, b, q / 2);
             }
             r.k1 = tok_kv(a, first + (q - P));
             r.s1 = tok_score(a, first + (q - P));
             r.latent_idx = nr;
+            r.token = -1;
             rows[nr] = r;
           }
           ++nr;
         }
-        if ((P + n - 1) % 2 == 0) {
+        int64_t last = P + n - 1;
+        if (last % 2 == 0) {
           if (sw) {
-            kvo_state_write w = {b, tok_kv(a, first + n - 1), tok_score(a, first + n - 1)};
+            kvo_state_write w = {state_kv(a, b, last / 2), state_score(a, b, last / 2),
+                                 tok_kv(a, first + n - 1), tok_score(a, first + n - 1)};
             sw[ns] = w;
           }
           ++ns;
         }
       }
     } else {
-      int64_t pos = a->start_pos[b];
-      if (pos < 0) continue;
-      if (a->ratio == 1) {
-        if (rows) {
-          kvo_row r = {b, pos, pos, NULL, NULL, tok_kv(a, b), tok_score(a, b), b};
-          rows[nr] = r;
+      const int64_t D = a->mode == KVO_VERIFY ? a->draft_len : 1;
+      int64_t P = a->start_pos[b];
+      if (P < 0) continue;
+      for (int64_t j = 0; j < D; ++j) {
+        int64_t q = P + j, t = (int64_t)b * D + j;
+        if (a->ratio == 1) {
+          if (rows) {
+            kvo_row r = {b, q, q, NULL, NULL, tok_kv(a, t), tok_score(a, t), t, t};
+            rows[nr] = r;
+          }
+          ++nr;
+        } else if (q % 2 == 1) {
+          if (rows) {
+            kvo_row r = {b, q / 2, q - 1, NULL, NULL, tok_kv(a, t), tok_score(a, t), t, t};
+            if (j > 0) {
+              r.k0 = tok_kv(a, t - 1);
+              r.s0 = tok_score(a, t - 1);
+            } else {
+              r.k0 = state_kv(a, b, q / 2);
+              r.s0 = state_score(a, b, q / 2);
+            }
+            rows[nr] = r;
+          }
+          ++nr;
+        } else {
+          if (sw) {
+            kvo_state_write w = {state_kv(a, b, q / 2), state_score(a, b, q / 2),
+                                 tok_kv(a, t), tok_score(a, t)};
+            sw[ns] = w;
+          }
+          ++ns;
         }
-        ++nr;
-      } else if (pos % 2 == 1) {
-        if (rows) {
-          kvo_row r = {b, pos / 2, pos - 1, state_kv(a, b), state_score(a, b),
-                       tok_kv(a, b), tok_score(a, b), b};
-          rows[nr] = r;
-        }
-        ++nr;
-      } else {
-        if (sw) {
-          kvo_state_write w = {b, tok_kv(a, b), tok_score(a, b)};
-          sw[ns] = w;
-        }
-        ++ns;
       }
     }
   }
@@ -575,14 +674,61 @@ void kvo_compress(const kvo_compress_args* a) {
       kvo_store_row(a->cache.layout, z, row_data(&a->cache, loc), row_scale(&a->cache, loc));
   }
 
-  /* pending-state writes come after every row that may read the old state */
+  /* pending-state writes come after every row that may read the old state,
+   * in token order (a later token of a slot overwrites an earlier one that
+   * shares its ring entry) */
   for (int64_t i = 0; i < ns; ++i) {
-    memcpy(state_kv(a, sw[i].slot), sw[i].kv, KVO_D * sizeof(uint16_t));
+    memcpy(sw[i].kv_dst, sw[i].kv, KVO_D * sizeof(uint16_t));
     if (sw[i].score)
-      memcpy(state_score(a, sw[i].slot), sw[i].score, KVO_D * sizeof(uint16_t));
+      memcpy(sw[i].score_dst, sw[i].score, KVO_D * sizeof(uint16_t));
   }
   free(rows);
   free(sw);
+}
+
+/* ------------------------------------------------------------------------
+ * One rank's share of global compressed ids [FI-dcp]: per token row t, the
+ * ids of request token_to_req[t] that this rank owns, in their order,
+ * mapped through the request's block-table row to this rank's physical
+ * slots, written as a prefix of out_slots[t] followed by -1, with the prefix
+ * length in out_lens[t].  Negative ids and other ranks' ids are dropped; a
+ * row whose `valid` entry is 0 (a graph padding token) keeps nothing.
+ * Readings: a request index outside the table drops the whole row
+ * (KVO_ST_REQ_RANGE); a page beyond the block-table row or outside the
+ * cache drops the id (KVO_ST_PT_RANGE / KVO_ST_PAGE_RANGE).  With world = 1
+ * this is the single-rank mapping with the -1 entries squeezed out.
+ * ---------------------------------------------------------------------- */
+void kvo_dcp_filter_ids(const int32_t* ids, int64_t T, int32_t k, int64_t ids_stride,
+                        const int32_t* token_to_req, int32_t n_req,
+                        const int32_t* block_table, int64_t bt_stride,
+                        const int32_t* valid, int32_t page_size, int64_t num_pages,
+                        int32_t world, int32_t rank, int32_t interleave,
+                        int32_t* out_slots, int64_t out_stride, int32_t* out_lens,
+                        int32_t* status) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    int32_t* o = out_slots + t * out_stride;
+    int32_t cnt = 0;
+    int32_t req = token_to_req[t];
+    int keep_row = !(valid && valid[t] == 0);
+    if (keep_row && (req < 0 || req >= n_req)) {
+      set_status(status, KVO_ST_REQ_RANGE);
+      keep_row = 0;
+    }
+    for (int32_t i = 0; keep_row && i < k; ++i) {
+      int64_t id = ids[t * ids_stride + i];
+      if (id < 0) continue;
+      int64_t local;
+      if (kvo_dcp_owner(id, world, interleave, &local) != rank) continue;
+      int64_t lp = local / page_size;
+      if (lp >= bt_stride) { set_status(status, KVO_ST_PT_RANGE); continue; }
+      int64_t phys = block_table[(int64_t)req * bt_stride + lp];
+      if (phys < 0 || phys >= num_pages) { set_status(status, KVO_ST_PAGE_RANGE); continue; }
+      o[cnt++] = (int32_t)(phys * page_size + local % page_size);
+    }
+    for (int32_t i = cnt; i < k; ++i) o[i] = -1;
+    out_lens[t] = cnt;
+  }
 }
 
 /* ------------------------------------------------------------------------

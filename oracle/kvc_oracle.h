@@ -27,6 +27,11 @@
  *  [PR45909-S]  sglang PR #45909, summary: reuse of one dequant per source.
  *  [FI-topk]    flashinfer_sparse.py, _compressed_topk_to_slots: request
  *               ids mapped to physical slots through the block table.
+ *  [FI-dcp]     flashinfer_sparse.py, DCP helpers (_compressed_topk_to_slots
+ *               for more than one rank, _dcp_prefill_gather): global
+ *               compressed ids dealt to the ranks in runs of the interleave
+ *               size, pages of block_size states per rank, the ids other
+ *               ranks own dropped and this rank's slots compacted to a prefix.
  * Where the pages leave a step open, the reading taken is stated beside the
  * function.  Functions whose exact results have no pin of their own say
  * "parity unpinned".
@@ -41,7 +46,7 @@ extern "C" {
 #endif
 
 enum { KVO_V4 = 0, KVO_V41 = 1, KVO_V41_FP4 = 2 };
-enum { KVO_PREFILL = 0, KVO_DECODE = 1 };
+enum { KVO_PREFILL = 0, KVO_DECODE = 1, KVO_VERIFY = 2 };
 
 /* status bits (the values documented for the device status word) */
 enum {
@@ -49,7 +54,8 @@ enum {
   KVO_ST_PAGE_RANGE = 2,    /* physical page outside the cache             */
   KVO_ST_PT_RANGE = 4,      /* compressed row beyond the slot's page table */
   KVO_ST_LATENT_RANGE = 8,  /* latent ordinal beyond the output capacity   */
-  KVO_ST_POS_RANGE = 16     /* rotary position outside the table           */
+  KVO_ST_POS_RANGE = 16,    /* rotary position outside the table           */
+  KVO_ST_REQ_RANGE = 32     /* request index outside the block table       */
 };
 
 typedef struct {
@@ -62,7 +68,7 @@ typedef struct {
 
 typedef struct {
   int32_t ratio;              /* 1 or 2 */
-  int32_t mode;               /* KVO_PREFILL or KVO_DECODE */
+  int32_t mode;               /* KVO_PREFILL, KVO_DECODE or KVO_VERIFY */
   const uint16_t* kv;         /* token rows, kv part (bf16) */
   int64_t kv_stride;          /* elements between token rows */
   const uint16_t* score;      /* token rows, score part (ratio 2) */
@@ -72,8 +78,9 @@ typedef struct {
   const int32_t* start_pos;   /* [S] position of the slot's first (or only) token */
   const int32_t* page_table;  /* [S, pt_stride] compressed-row pages, or NULL */
   int64_t pt_stride;
-  const int32_t* out_loc;     /* decode: [S] destination slot, 0 = no write; or NULL */
-  uint16_t* state;            /* [S, 2, 512] pending token (kv, score) for ratio 2 */
+  const int32_t* out_loc;     /* decode / verify: [S * draft_len] destination slot,
+                                 0 = no write; or NULL */
+  uint16_t* state;            /* [S, ring, 2, 512] pending tokens (kv, score), ratio 2 */
   const uint16_t* norm_w;     /* [512] bf16 */
   float eps;
   const float* freqs;         /* [max_pos, 64] fp32 (cos, sin) pairs */
@@ -85,6 +92,11 @@ typedef struct {
   int64_t prequant_stride;
   kvo_cache cache;
   int32_t* status;
+  int32_t draft_len;          /* verify: tokens per slot */
+  int32_t ring_slots;         /* pending-state entries per slot (<= 1: one) */
+  int32_t dcp_world;          /* context-parallel ranks (<= 1: none) */
+  int32_t dcp_rank;
+  int32_t dcp_interleave;     /* consecutive compressed rows per rank turn */
 } kvo_compress_args;
 
 /* layouts */
@@ -116,9 +128,26 @@ void kvo_dequant_gather(const kvo_cache* c, const int32_t* page_table,
                         int64_t n_pages, const int32_t* ids, int64_t n,
                         uint16_t* out, int64_t out_stride, int32_t* status);
 
+/* store with the rotary embedding applied first */
+void kvo_store_rows_rope(const kvo_cache* c, const uint16_t* rows, int64_t row_stride,
+                         const int32_t* positions, const float* freqs, int64_t max_pos,
+                         const int32_t* out_loc, int64_t n, uint16_t* rotated,
+                         int32_t* status);
+
 /* compressor */
 void kvo_compress(const kvo_compress_args* a);
 int64_t kvo_count_rows(const kvo_compress_args* a);
+
+/* decode context parallelism: owner rank and per-rank ordinal of a
+ * compressed row, and one rank's share of a list of global row ids */
+int32_t kvo_dcp_owner(int64_t c, int32_t world, int32_t interleave, int64_t* local);
+void kvo_dcp_filter_ids(const int32_t* ids, int64_t T, int32_t k, int64_t ids_stride,
+                        const int32_t* token_to_req, int32_t n_req,
+                        const int32_t* block_table, int64_t bt_stride,
+                        const int32_t* valid, int32_t page_size, int64_t num_pages,
+                        int32_t world, int32_t rank, int32_t interleave,
+                        int32_t* out_slots, int64_t out_stride, int32_t* out_lens,
+                        int32_t* status);
 
 /* array forms (for sweeps in tests) */
 void kvo_e4m3_encode_n(const double* v, int64_t n, int satfinite, uint8_t* out);

@@ -113,3 +113,20 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     """spacing of bf16 values at |x| (normal range)."""
     a = np.maximum(np.abs(x), 2.0 ** -126)
     return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def bf16_nearest(values) -> np.ndarray:
+    """bf16 bit patterns nearest to fp64 ``values`` by search over every
+    finite bf16 magnitude, ties to the even pattern; magnitudes past the
+    largest finite value by half its spacing or more become infinity."""
+    vals = np.asarray(values, np.float64)
+    pos = np.arange(0, 0x7F81, dtype=np.uint16)              # +0 .. +inf
+    g = bf16_value(pos)
+    g[-1] = 2.0 ** 128                                       # where infinity begins
+    mag = np.abs(vals)
+    hi = np.clip(np.searchsorted(g, mag, side="left"), 0, len(g) - 1)
+    lo = np.clip(hi - 1, 0, len(g) - 1)
+    dlo, dhi = np.abs(mag - g[lo]), np.abs(g[hi] - mag)
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & ((pos[hi] & 1) == 0) & (hi != lo))
+    code = np.where(pick_hi, pos[hi], pos[lo]).astype(np.uint16)
+    return code | np.where(np.signbit(vals), np.uint16(0x8000), np.uint16(0))

@@ -29,7 +29,8 @@ __all__ = [
     "D", "ROPE_DIMS", "BASE_SEED", "bf16_bits", "bf16_to_f32", "normal_bf16",
     "norm_weight", "rope_freqs", "outlier_rows", "random_pages",
     "paged_cache_shape", "random_cache_bytes", "compress_case", "decode_case",
-    "store_case", "gather_case", "ragged_lengths",
+    "store_case", "gather_case", "ragged_lengths", "verify_case", "rope_store_case",
+    "dcp_ids_case", "per_rank_page_tables",
     "workload_c1", "workload_c2", "workload_c3", "workload_c4", "workload_c5",
 ]
 
@@ -281,6 +282,101 @@ def gather_case(seed: int, logical_pages: int, page_size: int, n_ids: int,
     ids = rng.choice(logical_pages * page_size, size=n_ids, replace=False).astype(np.int32)
     return dict(cache=cache, page_table=page_table, ids=ids, num_pages=num_pages,
                 page_size=page_size, page_stride=stride)
+
+
+def verify_case(seed: int, batch: int, draft_len: int = 4, ratio: int = 2,
+                page_size: int = 16, max_pos: int = 512, ring_slots: int = 3,
+                explicit_out_loc: bool = False, skip_frac: float = 0.0,
+                pad_frac: float = 0.0625):
+    """Speculative-decoding verify inputs: ``batch`` slots with ``draft_len``
+    tokens each (token j of slot b is row ``b*draft_len + j`` of a fused
+    ``|kv|score|`` buffer), start positions uniform in [0, max_pos -
+    draft_len], a fraction ``skip_frac`` of slots with start position -1 and
+    a random pending-state ring ``[batch, ring_slots, 2, 512]``.
+
+    With ``explicit_out_loc`` every token gets its own destination slot
+    (distinct, pages 1..), a fraction ``pad_frac`` of them 0 (padded).
+    Otherwise each slot gets a page table of distinct random pages covering
+    every position below ``max_pos``."""
+    rng = np.random.default_rng(seed)
+    n_tok = batch * draft_len
+    pos = rng.integers(0, max_pos - draft_len + 1, size=batch).astype(np.int32)
+    if skip_frac > 0:
+        pos[rng.random(batch) < skip_frac] = -1
+    proj = normal_bf16(rng, (n_tok, 2 * D))
+    state = normal_bf16(rng, (batch, ring_slots, 2, D))
+    w = norm_weight(rng)
+    out_loc = page_table = None
+    if explicit_out_loc:
+        num_pages = n_tok // page_size + 3
+        slots = rng.permutation((num_pages - 1) * page_size)[:n_tok] + page_size
+        slots[rng.random(n_tok) < pad_frac] = 0
+        out_loc = slots.astype(np.int32)
+    else:
+        lp = (max_pos // ratio) // page_size + 1
+        num_pages = batch * lp + 1
+        page_table = random_pages(rng, batch * lp, num_pages).reshape(batch, lp)
+    return dict(ratio=ratio, kv=proj, pos=pos, out_loc=out_loc, page_table=page_table,
+                page_size=page_size, num_pages=num_pages, state=state, norm_w=w, eps=1e-6,
+                freqs=rope_freqs(max_pos), S=batch, draft_len=draft_len,
+                ring_slots=ring_slots)
+
+
+def rope_store_case(seed: int, lengths, page_size: int = 64, max_pos: int = 4096,
+                    pad_frac: float = 0.03, bad_pos_frac: float = 0.0):
+    """Store-with-RoPE inputs: ``store_case`` rows and slots plus a rotary
+    position per row (uniform in [0, max_pos)), a fraction ``pad_frac`` of
+    rows padded (out_loc 0) and a fraction ``bad_pos_frac`` given a position
+    outside the table."""
+    c = store_case(seed, lengths, page_size=page_size)
+    rng = np.random.default_rng(seed + 1)
+    n = c["rows"].shape[0]
+    pos = rng.integers(0, max_pos, size=n).astype(np.int32)
+    if bad_pos_frac > 0:
+        bad = rng.random(n) < bad_pos_frac
+        pos[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, max_pos + 7)
+    out_loc = c["out_loc"].copy()
+    out_loc[rng.random(n) < pad_frac] = 0
+    c.update(positions=pos, out_loc=out_loc, freqs=rope_freqs(max_pos))
+    return c
+
+
+def per_rank_page_tables(seed: int, world: int, slots: int, entries: int):
+    """One page table per rank of a context-parallel group: ``[world, slots,
+    entries]`` distinct random pages of that rank's own cache (never page
+    0); returns (tables, pages per rank cache)."""
+    rng = np.random.default_rng(seed)
+    num_pages = slots * entries + 1
+    t = np.stack([random_pages(rng, slots * entries, num_pages).reshape(slots, entries)
+                  for _ in range(world)])
+    return t, num_pages
+
+
+def dcp_ids_case(seed: int, T: int, k: int, n_req: int, max_rows: int, world: int,
+                 page_size: int, neg_frac: float = 0.05, invalid_frac: float = 0.05):
+    """Global compressed-row ids for a context-parallel gather: ``T`` token
+    rows (request of each row sorted, uniform over ``n_req`` requests), each
+    with ``k`` distinct ids below its request's row count (uniform in
+    [1, max_rows]) in random order, a fraction ``neg_frac`` replaced by -1
+    (and -1 wherever the request has fewer than k rows); per-rank block
+    tables ``[world, n_req, entries]`` of distinct random pages with
+    ``entries`` = max_rows // page_size + 1; a ``valid`` flag per row with
+    a fraction ``invalid_frac`` of zeros (graph padding tokens)."""
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(1, max_rows + 1, size=n_req)
+    t2r = np.sort(rng.integers(0, n_req, size=T)).astype(np.int32)
+    ids = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        n = int(rows[t2r[t]])
+        m = min(n, k)
+        ids[t, :m] = rng.choice(n, size=m, replace=False)
+        ids[t] = ids[t, rng.permutation(k)]
+    ids[rng.random((T, k)) < neg_frac] = -1
+    entries = max_rows // page_size + 1
+    bt, num_pages = per_rank_page_tables(seed + 1, world, n_req, entries)
+    valid = (rng.random(T) >= invalid_frac).astype(np.int32)
+    return dict(ids=ids, token_to_req=t2r, block_tables=bt, num_pages=num_pages,
+                valid=valid, rows=rows.astype(np.int32), page_size=page_size)
 
 
 # --------------------------------------------------------------------------
