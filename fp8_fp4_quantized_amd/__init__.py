@@ -23,9 +23,9 @@ LIB_PATH = os.path.join(HERE, "libkvc.so")
 KVC_OK, KVC_EINVAL, KVC_EUNSUPPORTED, KVC_ELAUNCH = 0, -1, -2, -3
 LAYOUT_V4, LAYOUT_V41, LAYOUT_V41_FP4 = 0, 1, 2
 LAYOUTS = {"V4": LAYOUT_V4, "V41": LAYOUT_V41, "V41_FP4": LAYOUT_V41_FP4}
-MODE_PREFILL, MODE_DECODE = 0, 1
+MODE_PREFILL, MODE_DECODE, MODE_VERIFY = 0, 1, 2
 STATUS_ID_RANGE, STATUS_PAGE_RANGE, STATUS_PT_RANGE = 1, 2, 4
-STATUS_LATENT_RANGE, STATUS_POS_RANGE = 8, 16
+STATUS_LATENT_RANGE, STATUS_POS_RANGE, STATUS_REQ_RANGE = 8, 16, 32
 
 
 class KvcError(RuntimeError):
@@ -58,6 +58,8 @@ class kvc_compress_args(C.Structure):
         ("latent_out", C.c_void_p), ("latent_stride", C.c_int64), ("max_out_rows", C.c_int64),
         ("prequant_out", C.c_void_p), ("prequant_stride", C.c_int64),
         ("cache", kvc_cache), ("status", C.c_void_p),
+        ("draft_len", C.c_int32), ("ring_slots", C.c_int32),
+        ("dcp_world", C.c_int32), ("dcp_rank", C.c_int32), ("dcp_interleave", C.c_int32),
     ]
 
 
@@ -66,6 +68,10 @@ _VP, _I32, _I64 = C.c_void_p, C.c_int32, C.c_int64
 SIGNATURES = {
     "kvc_layout_query": (C.c_int, [_I32, C.POINTER(kvc_layout_info)]),
     "kvc_store_rows": (C.c_int, [C.POINTER(kvc_cache), _VP, _I64, _VP, _I64, _VP, _VP]),
+    "kvc_store_rows_rope": (C.c_int, [C.POINTER(kvc_cache), _VP, _I64, _VP, _VP, _I64, _VP, _I64,
+                                      _VP, _VP]),
+    "kvc_dcp_filter_ids": (C.c_int, [_VP, _I64, _I32, _I64, _VP, _I32, _VP, _I64, _VP, _I32, _I64,
+                                     _I32, _I32, _I32, _VP, _I64, _VP, _VP, _VP]),
     "kvc_compress_store": (C.c_int, [C.POINTER(kvc_compress_args), _VP]),
     "kvc_dequant_gather": (C.c_int, [C.POINTER(kvc_cache), _VP, _I64, _VP, _I64, _VP, _I64, _VP, _VP]),
     "kvc_kvbuf_create": (_VP, []),
@@ -159,6 +165,34 @@ def kvc_store_rows(cache: Cache, rows: torch.Tensor, out_loc: torch.Tensor,
                                 rows.shape[0], _ptr(status), _stream(stream)))
 
 
+def kvc_store_rows_rope(cache: Cache, rows: torch.Tensor, positions: torch.Tensor,
+                        freqs: torch.Tensor, out_loc: torch.Tensor,
+                        status: torch.Tensor | None = None, stream=None) -> None:
+    """Rotate the rope dims of bf16 ``rows [n, >=512]`` at ``positions [n]``
+    (table ``freqs [max_pos, 64]`` fp32) and quantize them at ``out_loc``."""
+    d = cache.desc()
+    _check(lib().kvc_store_rows_rope(C.byref(d), rows.data_ptr(), rows.stride(0),
+                                     positions.data_ptr(), freqs.data_ptr(), freqs.shape[0],
+                                     out_loc.data_ptr(), rows.shape[0], _ptr(status),
+                                     _stream(stream)))
+
+
+def kvc_dcp_filter_ids(ids: torch.Tensor, token_to_req: torch.Tensor, block_table: torch.Tensor,
+                       out_slots: torch.Tensor, out_lens: torch.Tensor, *, page_size: int,
+                       num_pages: int, world: int, rank: int, interleave: int,
+                       valid: torch.Tensor | None = None, status: torch.Tensor | None = None,
+                       stream=None) -> None:
+    """This rank's share of global compressed ids ``[T, k]``: physical slots
+    compacted into ``out_slots [T, k]`` (-1 tail), counts into ``out_lens [T]``."""
+    T, k = ids.shape
+    _check(lib().kvc_dcp_filter_ids(ids.data_ptr(), T, k, ids.stride(0), token_to_req.data_ptr(),
+                                    block_table.shape[0], block_table.data_ptr(),
+                                    block_table.stride(0), _ptr(valid), page_size, num_pages,
+                                    world, rank, interleave, out_slots.data_ptr(),
+                                    out_slots.stride(0), out_lens.data_ptr(), _ptr(status),
+                                    _stream(stream)))
+
+
 def kvc_dequant_gather(cache: Cache, page_table: torch.Tensor | None, ids: torch.Tensor,
                        out: torch.Tensor, status: torch.Tensor | None = None, stream=None) -> None:
     """``out[j] = bf16 row of ids[j]`` (through ``page_table`` when given)."""
@@ -207,10 +241,12 @@ def kvc_compress_store(*, ratio: int, mode: int, kv: torch.Tensor, score: torch.
                        offsets: torch.Tensor | None = None, page_table: torch.Tensor | None = None,
                        out_loc: torch.Tensor | None = None, state: torch.Tensor | None = None,
                        prequant_out: torch.Tensor | None = None, status: torch.Tensor | None = None,
-                       stream=None) -> None:
+                       draft_len: int = 1, ring_slots: int = 1, dcp_world: int = 1,
+                       dcp_rank: int = 0, dcp_interleave: int = 1, stream=None) -> None:
     """The fused compressor.  ``kv``/``score`` are 2-D views whose row stride
     is passed through (a fused ``|kv|score|`` buffer ``proj [T, 1024]`` is
-    ``kv=proj[:, :512], score=proj[:, 512:]``)."""
+    ``kv=proj[:, :512], score=proj[:, 512:]``).  ``state`` is ``[S,
+    ring_slots, 2, 512]`` bf16 (``[S, 2, 512]`` for one entry)."""
     a = kvc_compress_args()
     a.ratio, a.mode = ratio, mode
     a.kv, a.kv_stride = kv.data_ptr(), kv.stride(0)
@@ -229,4 +265,6 @@ def kvc_compress_store(*, ratio: int, mode: int, kv: torch.Tensor, score: torch.
     a.prequant_stride = 0 if prequant_out is None else prequant_out.stride(0)
     a.cache = cache.desc()
     a.status = _ptr(status)
+    a.draft_len, a.ring_slots = draft_len, ring_slots
+    a.dcp_world, a.dcp_rank, a.dcp_interleave = dcp_world, dcp_rank, dcp_interleave
     _check(lib().kvc_compress_store(C.byref(a), _stream(stream)))

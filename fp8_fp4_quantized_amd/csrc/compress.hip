@@ -14,6 +14,12 @@
 // host-side knowledge of the row counts (and can be captured in a graph).  A
 // work item is a tile of consecutive compressed rows of one slot; a wave
 // issues the loads of all its rows before it finishes the first.
+//
+// Decode and verify batches give one wave per slot, which takes the slot's
+// tokens in order.  The ratio-2 pending tokens live in a per-slot ring (pair
+// k in entry k % ring_slots), and under decode context parallelism the rows
+// another rank owns are computed but not stored (flashinfer_sparse.py, DCP
+// helpers).
 #include "launch.hpp"
 #include "row_ops.hpp"
 
@@ -31,16 +37,25 @@ __device__ __forceinline__ void raise_status(int32_t* status, int32_t bit) {
 }
 
 // One compressed row.  Token rows are indices into the projection buffer;
-// `from_state` says the pair's first token is the slot's pending state.
+// `from_state` says the pair's first token is the pending-state entry
+// `st_row` (entries counted over all slots: slot b's ring starts at entry
+// b * ring_slots).
 struct RowJob {
   int64_t t1;             // second (or only) token of the row
   int64_t rot_pos;        // rotary position
   int64_t latent_idx;
   int64_t loc;            // destination slot in the cache (0: no write)
-  int32_t slot;
+  int64_t st_row;
   int32_t loc_err;        // status bit raised instead of the write (0: none)
   bool from_state;
 };
+
+// the pending-state entry of pair k of slot b: entry k % ring_slots of the
+// slot's ring (positions are int32, so k fits in 32 bits)
+__device__ __forceinline__ int64_t ring_row(const CompressParams& p, int32_t b, int64_t k) {
+  const uint32_t R = (uint32_t)p.ring_slots;
+  return (int64_t)b * R + (R == 1 ? 0 : (uint32_t)k % R);
+}
 
 // registers of one row's inputs: this lane's 16 B of the pair's kv and score
 // rows and (rope lanes) its 8 rotary-table entries
@@ -62,7 +77,7 @@ __device__ __forceinline__ RowIn load_row(const CompressParams& p, const RowJob&
   in.k0 = in.s0 = in.s1 = make_uint4(0u, 0u, 0u, 0u);
   if constexpr (RATIO == 2) {
     in.s1 = ld_u4_nt(p.score + j.t1 * p.score_stride + dim0);
-    const uint16_t* st = p.state + (int64_t)j.slot * 2 * kDim;
+    const uint16_t* st = p.state + j.st_row * 2 * kDim;
     const uint16_t* k0 = j.from_state ? st : p.kv + (j.t1 - 1) * p.kv_stride;
     const uint16_t* s0 = j.from_state ? st + kDim : p.score + (j.t1 - 1) * p.score_stride;
     in.k0 = ld_u4(k0 + dim0);
@@ -180,10 +195,30 @@ __device__ __forceinline__ void page_loc(const CompressParams& p, int32_t b, int
   loc = (phys << p.cache.page_bits) | (c & ((int64_t(1) << p.cache.page_bits) - 1));
 }
 
-// copy a token's kv and score rows into the slot's pending state
-__device__ __forceinline__ void write_state(const CompressParams& p, int32_t b, int64_t tok) {
+// the destination of row c of slot b on this rank: with the rows dealt over
+// a decode-context-parallel group in runs of K = 2^interleave_log2, run
+// c / K belongs to rank (c / K) % world, which keeps it as its row
+// (c / (K * world)) * K + c % K; rows of other ranks are not stored (loc 0)
+__device__ __forceinline__ void dest_loc(const CompressParams& p, int32_t b, int64_t c,
+                                         int64_t& loc, int32_t& err) {
+  if (p.dcp_world > 1) {
+    const int kl = p.dcp_interleave_log2;
+    const uint32_t run = (uint32_t)(c >> kl);
+    const uint32_t turn = run / (uint32_t)p.dcp_world;
+    if (run - turn * (uint32_t)p.dcp_world != (uint32_t)p.dcp_rank) {
+      loc = 0;
+      err = 0;
+      return;
+    }
+    c = ((int64_t)turn << kl) | (c & ((int64_t(1) << kl) - 1));
+  }
+  page_loc(p, b, c, loc, err);
+}
+
+// copy a token's kv and score rows into pending-state entry st_row
+__device__ __forceinline__ void write_state(const CompressParams& p, int64_t st_row, int64_t tok) {
   const int dim0 = kDimsPerLane * lane_id();
-  uint16_t* st = p.state + (int64_t)b * 2 * kDim;
+  uint16_t* st = p.state + st_row * 2 * kDim;
   const uint4 kvv = ld_u4_nt(p.kv + tok * p.kv_stride + dim0);
   const uint4 scv = ld_u4_nt(p.score + tok * p.score_stride + dim0);
   st_u4(st + dim0, kvv);
@@ -289,7 +324,7 @@ __device__ __forceinline__ void run_tile(const CompressParams& p, const PagedKV<
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
       const int64_t c = c_lo + r < c_hi ? c_lo + r : c_hi - 1;
-      j[r].slot = b;
+      j[r].st_row = 0;
       j[r].latent_idx = lat0 + (c - c0);
       if constexpr (RATIO == 1) {
         j[r].t1 = first + (c - P);
@@ -300,24 +335,37 @@ __device__ __forceinline__ void run_tile(const CompressParams& p, const PagedKV<
         j[r].t1 = first + (q - P);
         j[r].rot_pos = q - 1;
         j[r].from_state = q - 1 < P;             // first token precedes the extend
+        if (j[r].from_state) j[r].st_row = ring_row(p, b, c);
       }
       in[r] = load_row<RATIO>(p, j[r]);
     }
-    // the tile's rows share one page (aligned, no larger than a page): one
-    // page-table lookup, needed only when the rows are stored
-    int64_t loc0;
-    int32_t loc_err;
-    page_loc(p, b, c_lo, loc0, loc_err);
-    const int64_t page_base = loc0 - (c_lo & page_mask);
+    if (p.dcp_world > 1) {
+      // rows dealt over a context-parallel group: each row has its own owner
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
+        const int64_t c = c_lo + r < c_hi ? c_lo + r : c_hi - 1;
+        dest_loc(p, b, c, j[r].loc, j[r].loc_err);
+      }
+    } else {
+      // the tile's rows share one page (aligned, no larger than a page): one
+      // page-table lookup, needed only when the rows are stored
+      int64_t loc0;
+      int32_t loc_err;
+      page_loc(p, b, c_lo, loc0, loc_err);
+      const int64_t page_base = loc0 - (c_lo & page_mask);
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
+        j[r].loc_err = loc_err;
+        j[r].loc = loc_err ? 0 : page_base + ((c_lo + r) & page_mask);
+      }
+    }
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
-      j[r].loc_err = loc_err;
-      j[r].loc = loc_err ? 0 : page_base + ((c_lo + r) & page_mask);
       if (c_lo + r < c_hi) finish_row<L, RATIO>(p, kv, w, j[r], in[r]);
     }
   }
   if constexpr (RATIO == 2) {
-    if (kt == 0 && ((P + n) & 1)) write_state(p, b, first + n - 1);
+    if (kt == 0 && ((P + n) & 1)) write_state(p, ring_row(p, b, (P + n - 1) >> 1), first + n - 1);
   }
 }
 
@@ -395,37 +443,53 @@ __global__ __launch_bounds__(kBlock) void compress_prefill_kernel(CompressParams
   }
 }
 
+// Decode and verify: one wave per slot takes the slot's D tokens (D = 1 for
+// decode) in order, as D single decode tokens.  Rows first: a ratio-2 token
+// at an odd position pools with the previous draft token, or for the first
+// token with the ring entry an earlier call left; the ring entries are
+// written after every row of the slot has read its inputs.
 template <int L, int RATIO>
-__global__ __launch_bounds__(kBlock) void compress_decode_kernel(CompressParams p) {
+__global__ __launch_bounds__(kBlock) void compress_tokens_kernel(CompressParams p) {
   const PagedKV<L> kv{p.cache.base, p.cache.page_stride, p.cache.num_pages, p.cache.page_bits};
   const int lane = lane_id();
   const int64_t b64 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   if (b64 >= p.num_slots) return;
   const int32_t b = (int32_t)b64;
-  const int64_t pos = ld_ro(p.start_pos + b);
-  if (pos < 0) return;
-  if (RATIO == 2 && (pos & 1) == 0) {          // first token of a pair: keep it pending
-    write_state(p, b, b);
-    return;
-  }
+  const int64_t P = ld_ro(p.start_pos + b);
+  if (P < 0) return;
+  const int32_t D = p.draft_len;
+  const int64_t t0 = (int64_t)b * D;
   const uint4 wr = ld_u4(p.norm_w + kDimsPerLane * lane);
   const float w[8] = {bf16_lo(wr.x), bf16_hi(wr.x), bf16_lo(wr.y), bf16_hi(wr.y),
                       bf16_lo(wr.z), bf16_hi(wr.z), bf16_lo(wr.w), bf16_hi(wr.w)};
-  RowJob j;
-  j.slot = b;
-  j.latent_idx = b;
-  j.t1 = b;
-  j.from_state = RATIO == 2;
-  j.rot_pos = RATIO == 2 ? pos - 1 : pos;
-  const int64_t c = RATIO == 2 ? (pos >> 1) : pos;
-  // destination: the caller's out_loc (0 = padded row) or the page table
-  if (p.out_loc != nullptr) {
-    j.loc = ld_ro(p.out_loc + b);
-    j.loc_err = 0;
-  } else {
-    page_loc(p, b, c, j.loc, j.loc_err);
+  for (int32_t jj = 0; jj < D; ++jj) {
+    const int64_t q = P + jj;
+    if (RATIO == 2 && (q & 1) == 0) continue;    // first token of a pair: pending
+    RowJob j;
+    j.t1 = t0 + jj;
+    j.latent_idx = t0 + jj;
+    j.from_state = RATIO == 2 && jj == 0;
+    j.st_row = j.from_state ? ring_row(p, b, q >> 1) : 0;
+    j.rot_pos = RATIO == 2 ? q - 1 : q;
+    // destination: the caller's out_loc (0 = padded row) or the page table
+    if (p.out_loc != nullptr) {
+      j.loc = ld_ro(p.out_loc + t0 + jj);
+      j.loc_err = 0;
+    } else {
+      dest_loc(p, b, RATIO == 2 ? (q >> 1) : q, j.loc, j.loc_err);
+    }
+    finish_row<L, RATIO>(p, kv, w, j, load_row<RATIO>(p, j));
   }
-  finish_row<L, RATIO>(p, kv, w, j, load_row<RATIO>(p, j));
+  if constexpr (RATIO == 2) {
+    // an even position's token becomes the pending token of its pair, unless
+    // a later token of this call takes the same ring entry
+    const int64_t last_pair = (P + D - 1) >> 1;
+    for (int32_t jj = 0; jj < D; ++jj) {
+      const int64_t q = P + jj;
+      if ((q & 1) != 0 || (q >> 1) + p.ring_slots <= last_pair) continue;
+      write_state(p, ring_row(p, b, q >> 1), t0 + jj);
+    }
+  }
 }
 
 template <int L, int RATIO>
@@ -455,7 +519,7 @@ hipError_t launch_one(const CompressParams& p, hipStream_t stream) {
 #undef KVC_PREFILL_LAUNCH
   } else {
     const int blocks = (p.num_slots + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((compress_decode_kernel<L, RATIO>), dim3(blocks), dim3(kBlock), 0, stream, p);
+    hipLaunchKernelGGL((compress_tokens_kernel<L, RATIO>), dim3(blocks), dim3(kBlock), 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -99,7 +99,7 @@ struct kvc_kvbuf {
 
 extern "C" {
 
-int kvc_version(void) { return 1; }
+int kvc_version(void) { return 2; }
 
 const char* kvc_last_error(void) { return g_last_error.c_str(); }
 
@@ -145,6 +145,79 @@ int kvc_store_rows(const kvc_cache* cache, const void* rows_bf16, int64_t row_st
   return launched(kvc::launch_store_rows(p, static_cast<hipStream_t>(stream)), who);
 }
 
+int kvc_store_rows_rope(const kvc_cache* cache, const void* rows_bf16, int64_t row_stride,
+                        const int32_t* positions, const float* freqs, int64_t max_pos,
+                        const int32_t* out_loc, int64_t n, int32_t* status, void* stream) {
+  const char* who = "kvc_store_rows_rope";
+  kvc::StoreParams p{};
+  int rc = check_cache(cache, &p.cache, who);
+  if (rc) return rc;
+  if (n < 0) return fail(KVC_EINVAL, "%s: n < 0", who);
+  if (n == 0) return ok();
+  if (rows_bf16 == nullptr || out_loc == nullptr || positions == nullptr)
+    return fail(KVC_EINVAL, "%s: NULL rows, out_loc or positions", who);
+  if (!aligned16(rows_bf16) || !row_stride_ok(row_stride))
+    return fail(KVC_EINVAL, "%s: rows must be 16-byte aligned with row_stride >= 512, a multiple of 8", who);
+  if (freqs == nullptr || !aligned16(freqs) || max_pos < 1)
+    return fail(KVC_EINVAL, "%s: freqs must be non-NULL, 16-byte aligned, max_pos >= 1", who);
+  p.rows = static_cast<const uint16_t*>(rows_bf16);
+  p.row_stride = row_stride;
+  p.out_loc = out_loc;
+  p.n = n;
+  p.status = status;
+  p.positions = positions;
+  p.freqs = freqs;
+  p.max_pos = max_pos;
+  return launched(kvc::launch_store_rows(p, static_cast<hipStream_t>(stream)), who);
+}
+
+int kvc_dcp_filter_ids(const int32_t* ids, int64_t T, int32_t k, int64_t ids_stride,
+                       const int32_t* token_to_req, int32_t n_req, const int32_t* block_table,
+                       int64_t bt_stride, const int32_t* valid, int32_t page_size,
+                       int64_t num_pages, int32_t world, int32_t rank, int32_t interleave,
+                       int32_t* out_slots, int64_t out_stride, int32_t* out_lens,
+                       int32_t* status, void* stream) {
+  const char* who = "kvc_dcp_filter_ids";
+  if (T < 0 || k < 0 || k > 65536) return fail(KVC_EINVAL, "%s: T < 0 or k outside [0, 65536]", who);
+  if (T == 0) return ok();
+  if (page_size < 1 || page_size > 4096 || (page_size & (page_size - 1)) != 0)
+    return fail(KVC_EINVAL, "%s: page_size %d is not a power of two in [1, 4096]", who, page_size);
+  if (world < 1 || world > 1024 || rank < 0 || rank >= world)
+    return fail(KVC_EINVAL, "%s: world %d / rank %d (1 <= world <= 1024, 0 <= rank < world)", who,
+                world, rank);
+  if (interleave < 1 || page_size % interleave != 0)
+    return fail(KVC_EINVAL, "%s: interleave %d must be >= 1 and divide page_size %d", who,
+                interleave, page_size);
+  if (token_to_req == nullptr || out_lens == nullptr)
+    return fail(KVC_EINVAL, "%s: NULL token_to_req or out_lens", who);
+  if (k > 0 && (ids == nullptr || out_slots == nullptr || ids_stride < k || out_stride < k))
+    return fail(KVC_EINVAL, "%s: NULL ids or out_slots, or a row stride below k", who);
+  if (n_req < 0 || (n_req > 0 && (block_table == nullptr || bt_stride < 1)))
+    return fail(KVC_EINVAL, "%s: n_req < 0, or no block table", who);
+  if (num_pages < 1 || num_pages > ((int64_t)1 << 31) / page_size)
+    return fail(KVC_EINVAL, "%s: num_pages must be >= 1 with num_pages * page_size in int32", who);
+  kvc::DcpFilterParams p{};
+  p.ids = ids;
+  p.T = T;
+  p.k = k;
+  p.ids_stride = ids_stride;
+  p.token_to_req = token_to_req;
+  p.n_req = n_req;
+  p.block_table = block_table;
+  p.bt_stride = bt_stride;
+  p.valid = valid;
+  p.page_bits = page_bits_of(page_size);
+  p.num_pages = num_pages;
+  p.world = world;
+  p.rank = rank;
+  p.interleave_log2 = page_bits_of(interleave);
+  p.out_slots = out_slots;
+  p.out_stride = out_stride;
+  p.out_lens = out_lens;
+  p.status = status;
+  return launched(kvc::launch_dcp_filter(p, static_cast<hipStream_t>(stream)), who);
+}
+
 int kvc_dequant_gather(const kvc_cache* cache, const int32_t* page_table, int64_t n_pages,
                        const int32_t* ids, int64_t n, void* out_bf16, int64_t out_row_stride,
                        int32_t* status, void* stream) {
@@ -175,8 +248,19 @@ int kvc_compress_store(const kvc_compress_args* a, void* stream) {
   int rc = check_cache(&a->cache, &p.cache, who);
   if (rc) return rc;
   if (a->ratio != 1 && a->ratio != 2) return fail(KVC_EUNSUPPORTED, "%s: ratio %d (1 or 2)", who, a->ratio);
-  if (a->mode != KVC_MODE_PREFILL && a->mode != KVC_MODE_DECODE)
+  if (a->mode != KVC_MODE_PREFILL && a->mode != KVC_MODE_DECODE && a->mode != KVC_MODE_VERIFY)
     return fail(KVC_EUNSUPPORTED, "%s: mode %d", who, a->mode);
+  if (a->mode == KVC_MODE_VERIFY && (a->draft_len < 1 || a->draft_len > 64))
+    return fail(KVC_EINVAL, "%s: verify draft_len %d outside [1, 64]", who, a->draft_len);
+  if (a->ring_slots < 0 || a->ring_slots > 1024)
+    return fail(KVC_EINVAL, "%s: ring_slots %d outside [0, 1024]", who, a->ring_slots);
+  const int32_t world = a->dcp_world > 1 ? a->dcp_world : 1;
+  if (a->dcp_world < 0 || world > 1024 || a->dcp_rank < 0 || a->dcp_rank >= world)
+    return fail(KVC_EINVAL, "%s: dcp_world %d / dcp_rank %d (world <= 1024, 0 <= rank < world)",
+                who, a->dcp_world, a->dcp_rank);
+  if (world > 1 && (a->dcp_interleave < 1 || a->cache.page_size % a->dcp_interleave != 0))
+    return fail(KVC_EINVAL, "%s: dcp_interleave %d must be >= 1 and divide page_size %d", who,
+                a->dcp_interleave, a->cache.page_size);
   if (a->num_slots < 0) return fail(KVC_EINVAL, "%s: num_slots < 0", who);
   if (a->num_slots == 0) return ok();
   if (a->mode == KVC_MODE_PREFILL && a->num_slots > kvc::max_prefill_slots())
@@ -195,7 +279,7 @@ int kvc_compress_store(const kvc_compress_args* a, void* stream) {
     if (a->page_table == nullptr || a->pt_stride < 1)
       return fail(KVC_EINVAL, "%s: prefill needs a page table with pt_stride >= 1", who);
   } else if (a->out_loc == nullptr && (a->page_table == nullptr || a->pt_stride < 1)) {
-    return fail(KVC_EINVAL, "%s: decode needs out_loc or a page table", who);
+    return fail(KVC_EINVAL, "%s: decode and verify need out_loc or a page table", who);
   }
   if (a->norm_w == nullptr || !aligned16(a->norm_w)) return fail(KVC_EINVAL, "%s: norm_w NULL or misaligned", who);
   if (a->freqs == nullptr || !aligned16(a->freqs) || a->max_pos < 1)
@@ -217,7 +301,7 @@ int kvc_compress_store(const kvc_compress_args* a, void* stream) {
   p.start_pos = a->start_pos;
   p.page_table = a->page_table;
   p.pt_stride = a->page_table ? a->pt_stride : 0;
-  p.out_loc = a->mode == KVC_MODE_DECODE ? a->out_loc : nullptr;
+  p.out_loc = a->mode != KVC_MODE_PREFILL ? a->out_loc : nullptr;
   p.state = static_cast<uint16_t*>(a->state);
   p.norm_w = static_cast<const uint16_t*>(a->norm_w);
   p.eps = a->eps;
@@ -229,6 +313,11 @@ int kvc_compress_store(const kvc_compress_args* a, void* stream) {
   p.prequant = static_cast<uint16_t*>(a->prequant_out);
   p.prequant_stride = a->prequant_stride;
   p.status = a->status;
+  p.draft_len = a->mode == KVC_MODE_VERIFY ? a->draft_len : 1;
+  p.ring_slots = a->ring_slots > 1 ? a->ring_slots : 1;
+  p.dcp_world = world;
+  p.dcp_rank = world > 1 ? a->dcp_rank : 0;
+  p.dcp_interleave_log2 = world > 1 ? page_bits_of(a->dcp_interleave) : 0;
   return launched(kvc::launch_compress(p, static_cast<hipStream_t>(stream)), who);
 }
 

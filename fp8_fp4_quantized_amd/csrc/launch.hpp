@@ -22,6 +22,30 @@ struct StoreParams {
   const int32_t* out_loc;
   int64_t n;
   int32_t* status;
+  const int32_t* positions;    // rotary positions (NULL: plain store)
+  const float* freqs;          // [max_pos, 64]
+  int64_t max_pos;
+};
+
+struct DcpFilterParams {
+  const int32_t* ids;
+  int64_t T;
+  int32_t k;
+  int64_t ids_stride;
+  const int32_t* token_to_req;
+  int32_t n_req;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  const int32_t* valid;        // nullable
+  int32_t page_bits;
+  int64_t num_pages;
+  int32_t world;
+  int32_t rank;
+  int32_t interleave_log2;
+  int32_t* out_slots;
+  int64_t out_stride;
+  int32_t* out_lens;
+  int32_t* status;
 };
 
 struct GatherParams {
@@ -38,7 +62,7 @@ struct GatherParams {
 struct CompressParams {
   CacheView cache;
   int32_t ratio;
-  int32_t mode;                // 0 prefill, 1 decode
+  int32_t mode;                // 0 prefill, 1 decode, 2 verify
   const uint16_t* kv;
   int64_t kv_stride;
   const uint16_t* score;
@@ -60,6 +84,11 @@ struct CompressParams {
   uint16_t* prequant;
   int64_t prequant_stride;
   int32_t* status;
+  int32_t draft_len;           // tokens per slot in decode / verify (decode: 1)
+  int32_t ring_slots;          // pending-state entries per slot (>= 1)
+  int32_t dcp_world;           // context-parallel ranks (1: none)
+  int32_t dcp_rank;
+  int32_t dcp_interleave_log2; // log2 of the rows per rank turn
   int32_t tile_log2;           // set by the launcher: log2 of rows per prefill work item
 };
 
@@ -68,6 +97,7 @@ struct CompressParams {
 hipError_t launch_store_rows(const StoreParams& p, hipStream_t stream);
 hipError_t launch_dequant_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_compress(const CompressParams& p, hipStream_t stream);
+hipError_t launch_dcp_filter(const DcpFilterParams& p, hipStream_t stream);
 
 // largest num_slots a prefill compress accepts (its LDS tables)
 int max_prefill_slots();

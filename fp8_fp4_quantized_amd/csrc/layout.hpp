@@ -80,6 +80,7 @@ enum : int32_t {
   kStPtRange = 4,
   kStLatentRange = 8,
   kStPosRange = 16,
+  kStReqRange = 32,
 };
 
 }  // namespace kvc

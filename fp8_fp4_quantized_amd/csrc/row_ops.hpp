@@ -131,6 +131,60 @@ __device__ __forceinline__ void store_row_wave<kV41Fp4>(uint4 x, uint8_t* data, 
   if ((lane & 7) == 6) *(uint32_t*)(scale + 4 * (lane >> 3)) = sw;
 }
 
+// ------------------------------------------------------------------ exact RoPE
+// fp64 -> bf16, nearest even, with bf16 subnormals and overflow to infinity;
+// NaN gives 0x7FC0.  Integer rounding of the fp64 significand, so the result
+// does not depend on the float denormal mode.
+__device__ __forceinline__ uint32_t bf16_from_f64(double d) {
+  const uint64_t u = (uint64_t)__double_as_longlong(d);
+  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+  const uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
+  if (mag > 0x7FF0000000000000ull) return 0x7FC0u;
+  const int e = (int)(mag >> 52);               // fp64 biased exponent
+  const int E = e - 1023 + 127;                 // bf16 biased exponent
+  if (E >= 255) return sign | 0x7F80u;          // >= 2^128 (or infinity)
+  const uint64_t m = (mag & 0xFFFFFFFFFFFFFull) | (e != 0 ? (1ull << 52) : 0ull);
+  // keep 8 significant bits for a normal result; a subnormal result keeps
+  // the bits at or above 2^-133
+  const int drop = 45 + (E >= 1 ? 0 : 1 - E);
+  if (drop > 60) return sign;                   // below a quarter of 2^-133
+  const uint64_t r = m >> drop;
+  const uint64_t rem = m & ((1ull << drop) - 1);
+  const uint64_t half = 1ull << (drop - 1);
+  const uint32_t up = (rem > half || (rem == half && (r & 1))) ? 1u : 0u;
+  const uint32_t out = (E >= 1 ? ((uint32_t)(E - 1) << 7) : 0u) + (uint32_t)r + up;
+  return sign | (out >= 0x7F80u ? 0x7F80u : out);
+}
+
+// Rotate the row's 64 rope dims, (448 + 2j, 449 + 2j) by (cos, sin) =
+// (fr[2j], fr[2j + 1]), spreading them one dim per lane: lane l pulls the
+// bf16 pair of dim 448 + l from the rope lane that holds it, forms its
+// rotated value in fp64 (the products of a bf16 and an fp32 value are exact
+// there, so one rounding remains) and rounds it to bf16; the rope lanes then
+// pull the rotated pairs back.  Every lane of the wave must call this; the
+// nope lanes get x back.  fr: the position's 64 table entries.
+__device__ __forceinline__ uint4 rope_row_exact(uint4 x, const float* fr) {
+  const int lane = lane_id();
+  const int pair = lane >> 1;
+  const int src = kRopeLane0 + (pair >> 2);
+  const uint32_t w0 = (uint32_t)__shfl((int)x.x, src), w1 = (uint32_t)__shfl((int)x.y, src);
+  const uint32_t w2 = (uint32_t)__shfl((int)x.z, src), w3 = (uint32_t)__shfl((int)x.w, src);
+  const int k = pair & 3;
+  const uint32_t w = k == 0 ? w0 : (k == 1 ? w1 : (k == 2 ? w2 : w3));
+  const float f = fr[lane];
+  const float g = dpp_f32<kDppQuadXor1>(f);     // the other entry of the pair
+  const bool odd = (lane & 1) != 0;
+  const double a = (double)bf16_lo(w), b = (double)bf16_hi(w);
+  const double c = (double)(odd ? g : f), s = (double)(odd ? f : g);
+  const double o = odd ? a * s + b * c : a * c - b * s;
+  const uint32_t h = bf16_from_f64(o);
+  const uint32_t word = h | (dpp_u32<kDppQuadXor1>(h) << 16);   // even lanes: dims l, l + 1
+  const int base = 8 * (lane - kRopeLane0);
+  const uint32_t r0 = (uint32_t)__shfl((int)word, base), r1 = (uint32_t)__shfl((int)word, base + 2);
+  const uint32_t r2 = (uint32_t)__shfl((int)word, base + 4), r3 = (uint32_t)__shfl((int)word, base + 6);
+  return lane >= kRopeLane0 ? make_uint4(r0, r1, r2, r3) : x;
+}
+
 // ------------------------------------------------------------------ dequant
 __device__ __forceinline__ uint32_t bf16_top(float f) { return __float_as_uint(f) >> 16; }
 

@@ -26,22 +26,92 @@ __device__ __forceinline__ void raise_status(int32_t* status, int32_t bit) {
 }
 
 // ------------------------------------------------------------------ store
-template <int L>
+// ROPE: rotate the rope dims at positions[i] first (exact, one rounding).
+template <int L, bool ROPE>
 __global__ __launch_bounds__(kBlock) void store_rows_kernel(StoreParams p) {
   const PagedKV<L> kv = paged<L>(p.cache);
   const int lane = lane_id();
   const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   for (int64_t i = wave0; i < p.n; i += nwaves) {
-    const uint4 x = ld_u4_nt(p.rows + i * p.row_stride + kDimsPerLane * lane);
+    uint4 x = ld_u4_nt(p.rows + i * p.row_stride + kDimsPerLane * lane);
     const int64_t loc = uniform(p.out_loc[i]);
     bool write = loc != 0;
+    if constexpr (ROPE) {
+      if (write) {
+        const int64_t pos = ld_ro(p.positions + i);
+        if (pos < 0 || pos >= p.max_pos) {
+          raise_status(p.status, kStPosRange);
+          write = false;
+        } else {
+          x = rope_row_exact(x, p.freqs + pos * kRope);
+        }
+      }
+    }
     if (write && !kv.valid(loc)) {
       raise_status(p.status, kStPageRange);
       write = false;
     }
     const int64_t slot = write ? loc : 0;
     store_row_wave<L>(x, kv.data(slot), kv.scale(slot), write);
+  }
+}
+
+// ------------------------------------------------------------------ DCP ids
+// One wave per row of ids, 64 ids per step: each lane tests its id for
+// ownership and maps it to a slot, a ballot and a lane count give every kept
+// id its place after the ones before it, and the row is finished with -1.
+__global__ __launch_bounds__(kBlock) void dcp_filter_kernel(DcpFilterParams p) {
+  const int lane = lane_id();
+  const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const int kl = p.interleave_log2;
+  const uint32_t kmask = (1u << kl) - 1, pmask = (1u << p.page_bits) - 1;
+  const uint32_t world = (uint32_t)p.world, rank = (uint32_t)p.rank;
+  for (int64_t t = wave0; t < p.T; t += nwaves) {
+    int32_t cnt = 0;
+    bool keep = p.valid == nullptr || ld_ro(p.valid + t) != 0;
+    const int32_t req = ld_ro(p.token_to_req + t);
+    if (keep && (req < 0 || req >= p.n_req)) {
+      raise_status(p.status, kStReqRange);
+      keep = false;
+    }
+    int32_t* out = p.out_slots + t * p.out_stride;
+    if (keep) {
+      const int32_t* row = p.ids + t * p.ids_stride;
+      const int32_t* bt = p.block_table + (int64_t)req * p.bt_stride;
+      for (int32_t i0 = 0; i0 < p.k; i0 += kLanes) {
+        const int32_t i = i0 + lane;
+        int32_t slot = -1, bad = 0;
+        const int32_t id = i < p.k ? row[i] : -1;
+        if (id >= 0) {
+          const uint32_t run = (uint32_t)id >> kl;
+          const uint32_t turn = run / world;
+          if (run - turn * world == rank) {
+            const uint32_t u = (turn << kl) | ((uint32_t)id & kmask);
+            const int64_t lp = u >> p.page_bits;
+            if (lp >= p.bt_stride) {
+              bad = kStPtRange;
+            } else {
+              const int32_t phys = bt[lp];
+              if (phys < 0 || phys >= p.num_pages) {
+                bad = kStPageRange;
+              } else {
+                slot = (phys << p.page_bits) | (int32_t)(u & pmask);
+              }
+            }
+          }
+        }
+        if (bad != 0 && p.status != nullptr) atomicOr(p.status, bad);
+        const uint64_t m = __ballot(slot >= 0);
+        const int32_t before = (int32_t)__builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (slot >= 0) out[cnt + before] = slot;
+        cnt += (int32_t)__builtin_popcountll(m);
+      }
+    }
+    for (int32_t i = cnt + lane; i < p.k; i += kLanes) out[i] = -1;
+    if (lane == 0) p.out_lens[t] = cnt;
   }
 }
 
@@ -189,11 +259,22 @@ LaunchTuning& launch_tuning() {
 
 hipError_t launch_store_rows(const StoreParams& p, hipStream_t stream) {
   const int blocks = grid_for(p.n, kWavesPerBlock, 8192);
+  const bool rope = p.positions != nullptr;
   switch (p.cache.layout) {
-    case kV41: return launch(store_rows_kernel<kV41>, blocks, p, stream);
-    case kV41Fp4: return launch(store_rows_kernel<kV41Fp4>, blocks, p, stream);
-    default: return launch(store_rows_kernel<kV4>, blocks, p, stream);
+    case kV41:
+      return rope ? launch(store_rows_kernel<kV41, true>, blocks, p, stream)
+                  : launch(store_rows_kernel<kV41, false>, blocks, p, stream);
+    case kV41Fp4:
+      return rope ? launch(store_rows_kernel<kV41Fp4, true>, blocks, p, stream)
+                  : launch(store_rows_kernel<kV41Fp4, false>, blocks, p, stream);
+    default:
+      return rope ? launch(store_rows_kernel<kV4, true>, blocks, p, stream)
+                  : launch(store_rows_kernel<kV4, false>, blocks, p, stream);
   }
+}
+
+hipError_t launch_dcp_filter(const DcpFilterParams& p, hipStream_t stream) {
+  return launch(dcp_filter_kernel, grid_for(p.T, kWavesPerBlock, 4096), p, stream);
 }
 
 hipError_t launch_dequant_gather(const GatherParams& p, hipStream_t stream) {

@@ -23,7 +23,12 @@
  *    forgotten on a plain get, a reallocation or a new forward.
  *  - flashinfer_sparse.py (vLLM DeepSeek-V4.1 sparse MLA backend),
  *    _compressed_topk_to_slots: request-local compressed ids mapped to
- *    physical slots through the block table, -1 marking empty entries.
+ *    physical slots through the block table, -1 marking empty entries; its
+ *    DCP helpers (the same function for more than one rank, and
+ *    _dcp_prefill_gather): global compressed ids dealt to the ranks of a
+ *    decode-context-parallel group in runs of the interleave size, pages of
+ *    block_size states per rank, the other ranks' ids dropped and this
+ *    rank's slots compacted to a prefix.
  *
  * Conventions shared by every entry point
  *  - Pointers named "device" are HIP device memory (or memory the device can
@@ -65,7 +70,8 @@ enum {
   KVC_STATUS_PAGE_RANGE = 2,   /* physical page < 0 or >= num_pages                       */
   KVC_STATUS_PT_RANGE = 4,     /* compressed row beyond its slot's page-table row          */
   KVC_STATUS_LATENT_RANGE = 8, /* latent row index >= max_out_rows                         */
-  KVC_STATUS_POS_RANGE = 16    /* rotary position < 0 or >= max_pos: row skipped           */
+  KVC_STATUS_POS_RANGE = 16,   /* rotary position < 0 or >= max_pos: row skipped           */
+  KVC_STATUS_REQ_RANGE = 32    /* request index outside the block table: row dropped        */
 };
 
 /* ---------------------------------------------------------------- layouts
@@ -133,6 +139,22 @@ int kvc_layout_query(int32_t layout, kvc_layout_info* info);
 int kvc_store_rows(const kvc_cache* cache, const void* rows_bf16, int64_t row_stride,
                    const int32_t* out_loc, int64_t n, int32_t* status, void* stream);
 
+/* kvc_store_rows with the rotary embedding applied in the kernel (sglang PR
+ * #39652, Summary: the cache writer with an optional in-kernel RoPE for the
+ * V4.1 layouts; accepted for every layout here).  Before row i is quantized,
+ * its dims (448 + 2j, 449 + 2j), j = 0..31, are rotated by (cos, sin) =
+ * (freqs[positions[i]][2j], freqs[positions[i]][2j + 1]); the products are
+ * formed in fp64 and the rotated value is rounded once to bf16 (nearest
+ * even), so the result does not depend on the evaluation order.  The other
+ * dims are stored as given.
+ *   positions  device int32 [n]; a position < 0 or >= max_pos skips the row
+ *              with KVC_STATUS_POS_RANGE (checked after out_loc == 0)
+ *   freqs      device fp32 [max_pos, 64], 16-byte aligned
+ * Other arguments and rules as kvc_store_rows. */
+int kvc_store_rows_rope(const kvc_cache* cache, const void* rows_bf16, int64_t row_stride,
+                        const int32_t* positions, const float* freqs, int64_t max_pos,
+                        const int32_t* out_loc, int64_t n, int32_t* status, void* stream);
+
 /* ---------------------------------------------------------------- compress
  * The ratio-1 / ratio-2 compressor (sglang PR #39652, Summary; sglang PR
  * #46230, summary), per output row:
@@ -171,8 +193,40 @@ int kvc_store_rows(const kvc_cache* cache, const void* rows_bf16, int64_t row_st
  *   given (0 = no cache write, a padded row), otherwise from the page table
  *   as in prefill.  The latent row of slot b is b (written only when a row is
  *   emitted).
+ * VERIFY mode (speculative decoding: draft_len = D tokens per slot; sglang
+ *   PR #39652, Summary and Review, the decode-or-verify ratio-2 compressor):
+ *   slot b's tokens are rows b*D .. b*D + D - 1 at positions start_pos[b] ..
+ *   start_pos[b] + D - 1 (start_pos[b] < 0: the slot is skipped), taken in
+ *   order as D decode tokens: token j's latent row and out_loc entry are
+ *   b*D + j, and a ratio-2 token at an odd position pools with the previous
+ *   draft token (j > 0) or with the ring entry (j = 0).  DECODE is VERIFY
+ *   with D = 1.
+ *
+ * Pending-state ring (ratio 2, every mode): state holds ring_slots entries
+ * per slot, entry e of slot b at state + (b*ring_slots + e)*1024 elements
+ * (kv then score, 512 each); the pending first token of pair k (positions
+ * 2k, 2k + 1) lives in entry k % ring_slots.  One entry is the plain decode
+ * state.  A verify step that accepts only the first a drafts is followed by
+ * a step at start_pos + a; that step finds its pending token intact when
+ * ring_slots > D / 2 (the entries one step writes then never reach the one
+ * an earlier step left).  When two even positions of one call share an
+ * entry, the later token's is the one written.
+ *
+ * Decode context parallelism (dcp_world W > 1; flashinfer_sparse.py, DCP
+ * helpers): the compressed rows of a request are dealt to the W ranks in
+ * runs of dcp_interleave (K) consecutive rows, round robin (row c belongs to
+ * rank (c / K) % W), and every rank keeps its own rows densely: row c is the
+ * u-th row of its rank, u = (c / (K*W))*K + c % K, stored through this
+ * rank's page table at page_table[b][u / page_size] * page_size + u %
+ * page_size.  This call stores only the rows of rank dcp_rank; the other
+ * rows are still computed and their latent rows written.  page_size must be
+ * a multiple of K.  An explicit out_loc (decode, verify) is used as given.
  */
-typedef enum kvc_mode { KVC_MODE_PREFILL = 0, KVC_MODE_DECODE = 1 } kvc_mode;
+typedef enum kvc_mode {
+  KVC_MODE_PREFILL = 0,
+  KVC_MODE_DECODE = 1,
+  KVC_MODE_VERIFY = 2
+} kvc_mode;
 
 typedef struct kvc_compress_args {
   int32_t ratio;              /* 1 or 2 */
@@ -187,8 +241,8 @@ typedef struct kvc_compress_args {
   const int32_t* page_table;  /* device int32 [S, pt_stride]; may be NULL only
                                  in decode mode with out_loc */
   int64_t pt_stride;          /* entries per page-table row */
-  const int32_t* out_loc;     /* device int32 [S], decode only, or NULL */
-  void* state;                /* device bf16 [S, 2, 512]: pending (kv, score), ratio 2 */
+  const int32_t* out_loc;     /* device int32 [S * D], decode / verify only, or NULL */
+  void* state;                /* device bf16 [S, ring_slots, 2, 512]: pending (kv, score), ratio 2 */
   const void* norm_w;         /* device bf16 [512] */
   float eps;
   const float* freqs;         /* device fp32 [max_pos, 64] */
@@ -200,6 +254,11 @@ typedef struct kvc_compress_args {
   int64_t prequant_stride;
   kvc_cache cache;
   int32_t* status;            /* device int32 or NULL */
+  int32_t draft_len;          /* VERIFY: tokens per slot, 1..64 (other modes: ignored) */
+  int32_t ring_slots;         /* pending-state entries per slot, 1..1024 (0: 1) */
+  int32_t dcp_world;          /* decode-context-parallel ranks, 0 or 1: none; <= 1024 */
+  int32_t dcp_rank;           /* 0 .. dcp_world - 1 */
+  int32_t dcp_interleave;     /* consecutive rows per rank turn, >= 1, divides page_size */
 } kvc_compress_args;
 
 int kvc_compress_store(const kvc_compress_args* args, void* stream);
@@ -221,6 +280,39 @@ int kvc_compress_store(const kvc_compress_args* args, void* stream);
  * bf16.  A NaN code, a ue8m0 byte of 255 or a NaN e4m3 scale gives NaN. */
 int kvc_dequant_gather(const kvc_cache* cache, const int32_t* page_table, int64_t n_pages,
                        const int32_t* ids, int64_t n, void* out_bf16, int64_t out_row_stride,
+                       int32_t* status, void* stream);
+
+/* ---------------------------------------------------------------- DCP ids
+ * One rank's share of the gather ids of a decode-context-parallel group
+ * (flashinfer_sparse.py, DCP helpers: the ids of the indexer are GLOBAL
+ * compressed row ids; the states other ranks own are dropped and this rank's
+ * slots compacted to a prefix with a -1 tail and a count).  Row t of `ids`
+ * (k ids at ids + t*ids_stride) belongs to request token_to_req[t].  Each id
+ * c >= 0 that rank `rank` owns (the dealing of kvc_compress_store: run c / K
+ * goes to rank (c / K) % world; this rank's ordinal u = (c / (K*world))*K +
+ * c % K) becomes the physical slot block_table[req][u / page_size] *
+ * page_size + u % page_size.  The slots of a row are written, in the order
+ * of their ids, to out_slots + t*out_stride, followed by -1 up to k entries;
+ * out_lens[t] = their count.  The output is a physical-slot id list for
+ * kvc_dequant_gather with page_table = NULL.
+ *   ids          device int32, rows of k entries, ids_stride >= k
+ *   token_to_req device int32 [T]; a request outside [0, n_req) drops the
+ *                row (count 0) with KVC_STATUS_REQ_RANGE
+ *   block_table  device int32 [n_req, bt_stride]: this rank's pages
+ *   valid        device int32 [T] or NULL; 0 = a padding token: count 0
+ *   out_slots    device int32, out_stride >= k; must not overlap ids (may be
+ *                NULL when k = 0)
+ *   out_lens     device int32 [T]
+ * A page index >= bt_stride (KVC_STATUS_PT_RANGE) or a page < 0 or >=
+ * num_pages (KVC_STATUS_PAGE_RANGE) drops that id.  world = 1 (rank 0) maps
+ * through the block table with the -1 entries squeezed out.  page_size is a
+ * power of two in [1, 4096] and a multiple of interleave; 1 <= world <= 1024;
+ * 0 <= k <= 65536. */
+int kvc_dcp_filter_ids(const int32_t* ids, int64_t T, int32_t k, int64_t ids_stride,
+                       const int32_t* token_to_req, int32_t n_req, const int32_t* block_table,
+                       int64_t bt_stride, const int32_t* valid, int32_t page_size,
+                       int64_t num_pages, int32_t world, int32_t rank, int32_t interleave,
+                       int32_t* out_slots, int64_t out_stride, int32_t* out_lens,
                        int32_t* status, void* stream);
 
 /* ---------------------------------------------------------------- reuse
@@ -251,7 +343,7 @@ int kvc_dequant_gather_reuse(kvc_kvbuf* kb, const kvc_cache* cache, const int32_
 /* Message of the last failed call on this thread ("" if none). */
 const char* kvc_last_error(void);
 
-/* Library ABI version (this header: 1). */
+/* Library ABI version (this header: 2). */
 int kvc_version(void);
 
 /* Launch-shape knob for tuning: the number of workgroups of the gather grid,

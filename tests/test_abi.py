@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(kvc):
 
 
 def test_version_and_layouts(kvc):
-    assert kvc.kvc_version() == 1
+    assert kvc.kvc_version() == 2
     want = {"V4": (576, 8, 584, 64, 448), "V41": (512, 16, 528, 32, 512),
             "V41_FP4": (256, 32, 288, 16, 512)}
     for name, w in want.items():
@@ -95,6 +95,37 @@ def test_store_and_gather_argument_checks(kvc):
     assert L.kvc_dequant_gather(C.byref(c), FAKE, 0, FAKE, 5, FAKE, 512, None, None) == kvc.KVC_EINVAL
     assert L.kvc_dequant_gather(C.byref(c), None, 0, FAKE, 5, FAKE, 500, None, None) == kvc.KVC_EINVAL
     assert L.kvc_dequant_gather(C.byref(c), None, 0, FAKE, 5, FAKE + 8, 512, None, None) == kvc.KVC_EINVAL
+    # the rotary store: same checks plus positions and the table
+    rope = L.kvc_store_rows_rope
+    assert rope(C.byref(c), FAKE, 512, FAKE, FAKE, 16, FAKE, 0, None, None) == kvc.KVC_OK
+    assert rope(C.byref(c), FAKE, 512, None, FAKE, 16, FAKE, 3, None, None) == kvc.KVC_EINVAL
+    assert rope(C.byref(c), FAKE, 512, FAKE, None, 16, FAKE, 3, None, None) == kvc.KVC_EINVAL
+    assert rope(C.byref(c), FAKE, 512, FAKE, FAKE + 4, 16, FAKE, 3, None, None) == kvc.KVC_EINVAL
+    assert rope(C.byref(c), FAKE, 512, FAKE, FAKE, 0, FAKE, 3, None, None) == kvc.KVC_EINVAL
+    assert rope(C.byref(c), FAKE, 500, FAKE, FAKE, 16, FAKE, 3, None, None) == kvc.KVC_EINVAL
+    assert rope(C.byref(_cache(kvc, page_size=3)), FAKE, 512, FAKE, FAKE, 16, FAKE, 3, None,
+                None) == kvc.KVC_EINVAL
+
+
+def test_dcp_filter_argument_checks(kvc):
+    L = kvc.lib()
+
+    def call(T=4, k=8, ids_stride=8, t2r=FAKE, n_req=2, bt=FAKE, bt_stride=4, valid=None,
+             page_size=64, num_pages=10, world=2, rank=1, inter=4, out=FAKE, out_stride=8,
+             lens=FAKE):
+        return L.kvc_dcp_filter_ids(FAKE, T, k, ids_stride, t2r, n_req, bt, bt_stride, valid,
+                                    page_size, num_pages, world, rank, inter, out, out_stride,
+                                    lens, None, None)
+
+    assert call(T=0) == kvc.KVC_OK
+    for kw in (dict(T=-1), dict(k=-1), dict(k=65537, ids_stride=65537, out_stride=65537),
+               dict(page_size=48), dict(page_size=8192), dict(world=0), dict(world=1025),
+               dict(rank=2), dict(rank=-1), dict(inter=0), dict(inter=3), dict(inter=128),
+               dict(t2r=None), dict(out=None), dict(lens=None), dict(ids_stride=7),
+               dict(out_stride=4), dict(n_req=-1), dict(bt=None), dict(bt_stride=0),
+               dict(num_pages=0), dict(num_pages=1 << 30)):
+        assert call(**kw) == kvc.KVC_EINVAL, kw
+        assert kvc.kvc_last_error()
 
 
 def _args(kvc, **kw):
@@ -126,9 +157,22 @@ def test_compress_argument_checks(kvc):
     for kw in (dict(ratio=3), dict(ratio=0), dict(mode=5)):
         a = _args(kvc, **kw)
         assert L.kvc_compress_store(C.byref(a), None) == kvc.KVC_EUNSUPPORTED, kw
-    # decode needs out_loc or a page table
+    # decode and verify need out_loc or a page table
     a = _args(kvc, mode=kvc.MODE_DECODE, page_table=0, out_loc=0)
     assert L.kvc_compress_store(C.byref(a), None) == kvc.KVC_EINVAL
+    a = _args(kvc, mode=kvc.MODE_VERIFY, draft_len=4, page_table=0, out_loc=0)
+    assert L.kvc_compress_store(C.byref(a), None) == kvc.KVC_EINVAL
+    # verify draft length, ring size and the context-parallel group
+    for kw in (dict(mode=kvc.MODE_VERIFY, draft_len=0), dict(mode=kvc.MODE_VERIFY, draft_len=65),
+               dict(ring_slots=-1), dict(ring_slots=1025), dict(dcp_world=-1),
+               dict(dcp_world=2, dcp_rank=2, dcp_interleave=1),
+               dict(dcp_world=2, dcp_rank=-1, dcp_interleave=1),
+               dict(dcp_world=1025, dcp_rank=0, dcp_interleave=1),
+               dict(dcp_world=2, dcp_rank=0, dcp_interleave=0),
+               dict(dcp_world=2, dcp_rank=0, dcp_interleave=3),
+               dict(dcp_world=2, dcp_rank=0, dcp_interleave=256)):
+        a = _args(kvc, **kw)
+        assert L.kvc_compress_store(C.byref(a), None) == kvc.KVC_EINVAL, kw
     # nothing to do is fine
     a = _args(kvc, num_slots=0)
     assert L.kvc_compress_store(C.byref(a), None) == kvc.KVC_OK

@@ -1,0 +1,347 @@
+"""HIP path vs the oracle for the verify mode and pending-state ring, decode
+context parallelism (owner predicate in the compressor, id filter), the
+RoPE store and graph capture of the prefill compressor.
+
+Bar: bit-exact for bytes and indices (RoPE store bytes, filtered slots and
+counts, pending state, untouched cache bytes, the quantizer given the
+kernel's own pre-quant rows); 2e-2 relative, codes within one step, for the
+fused compressor's outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import spec
+from tests.gpu_util import (assert_latent_close, assert_rows_close, check_compress, dev, host,
+                            row_parts, run_compress, written_mask)
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = ["V4", "V41", "V41_FP4"]
+
+
+@pytest.fixture(scope="module")
+def K():
+    import fp8_fp4_quantized_amd as k
+    return k
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _token_rows(case, ratio, world=1, rank=0, interleave=1):
+    """(latent index, destination slot) of every token that emits a row in a
+    decode / verify batch; slot 0 where nothing is stored."""
+    S, D, ps = case["S"], case["draft_len"], case["page_size"]
+    lat, slots = [], []
+    for b in range(S):
+        p0 = int(case["pos"][b])
+        if p0 < 0:
+            continue
+        for j in range(D):
+            q, t = p0 + j, b * D + j
+            if ratio == 2 and q % 2 == 0:
+                continue
+            c = q // 2 if ratio == 2 else q
+            if case["out_loc"] is not None:
+                slot = int(case["out_loc"][t])
+            else:
+                r, u = oracle.dcp_owner(c, world, interleave)
+                slot = int(case["page_table"][b, u // ps]) * ps + u % ps if r == rank else 0
+            lat.append(t)
+            slots.append(slot)
+    return lat, slots
+
+
+# ================================================================= verify
+@pytest.mark.parametrize("explicit", [False, True])
+@pytest.mark.parametrize("layout,ratio", [("V41", 2), ("V41_FP4", 2), ("V4", 2), ("V41", 1)])
+def test_verify_batch(K, layout, ratio, explicit):
+    """draft_len 4, ring of 3 entries, skipped slots, padded tokens."""
+    _say("verify", layout, ratio, explicit)
+    case = W.verify_case(200 + ratio, 96, draft_len=4, ratio=ratio, page_size=16, max_pos=512,
+                         ring_slots=3, explicit_out_loc=explicit, skip_frac=0.1)
+    r = run_compress(K, case, layout, ratio, oracle.VERIFY, out_loc=case["out_loc"],
+                     page_table=case["page_table"], draft_len=4, ring_slots=3)
+    lat, slots = _token_rows(case, ratio)
+    assert r["n_rows"] == len(lat)
+    check_compress(r, layout, 16, slots, lat)
+
+
+@pytest.mark.parametrize("D,R", [(1, 1), (2, 2), (7, 4), (16, 1)])
+def test_verify_draft_lengths_and_rings(K, D, R):
+    """other draft lengths, a ring too small for rollback (still exact for
+    one call: the last token sharing an entry wins) and plain decode."""
+    _say("verify D R", D, R)
+    case = W.verify_case(210 + D, 40, draft_len=D, ratio=2, page_size=8, max_pos=300,
+                         ring_slots=R)
+    r = run_compress(K, case, "V41_FP4", 2, oracle.VERIFY, page_table=case["page_table"],
+                     draft_len=D, ring_slots=R)
+    lat, slots = _token_rows(case, 2)
+    check_compress(r, "V41_FP4", 8, slots, lat)
+
+
+def test_verify_rejection_steps(K):
+    """Nine verify steps with random acceptance on device and in the oracle:
+    every step's rows and the ring match; the ring restarts each step where
+    the accepted drafts end."""
+    _say("verify rejection steps")
+    D, S, ps, layout = 4, 64, 8, "V41"
+    base = W.verify_case(220, S, draft_len=D, page_size=ps, max_pos=64, ring_slots=3)
+    rb = oracle.layout_bytes(layout)[2]
+    hc = np.zeros((base["num_pages"], ps * rb), np.uint8)
+    dc = dev(hc)
+    st_h = np.zeros((S, 3, 2, 512), np.uint16)
+    st_d = dev(st_h)
+    pos = np.zeros(S, np.int32)
+    rng = np.random.default_rng(221)
+    written = set()
+    for step in range(9):
+        kv = W.normal_bf16(rng, (S * D, 1024))
+        case = dict(base, kv=kv, pos=pos.copy())
+        lat_o, pre_o, st_o, n = oracle.compress(
+            ratio=2, mode=oracle.VERIFY, kv=kv, fused=True, start_pos=pos,
+            page_table=base["page_table"], state=st_h, norm_w=base["norm_w"], eps=base["eps"],
+            freqs=base["freqs"], cache=hc, layout=layout, page_size=ps, draft_len=D,
+            ring_slots=3)
+        lat = torch.zeros((S * D, 512), dtype=torch.int16, device="cuda")
+        pre = torch.zeros_like(lat)
+        s = torch.zeros(1, dtype=torch.int32, device="cuda")
+        kvd = dev(kv)
+        K.kvc_compress_store(ratio=2, mode=K.MODE_VERIFY, kv=kvd[:, :512], score=kvd[:, 512:],
+                             start_pos=dev(pos), cache=K.Cache(dc, layout, ps),
+                             norm_w=dev(base["norm_w"]), eps=base["eps"],
+                             freqs=dev(base["freqs"]), latent_out=lat,
+                             page_table=dev(base["page_table"]), state=st_d, prequant_out=pre,
+                             status=s, draft_len=D, ring_slots=3)
+        torch.cuda.synchronize()
+        assert int(s.item()) == st_o == 0
+        assert np.array_equal(host(st_d, np.uint16), st_h), step
+        idx, slots = _token_rows(case, 2)
+        lat_g, pre_g = host(lat, np.uint16), host(pre, np.uint16)
+        assert_latent_close(lat_g[idx], lat_o[idx])
+        cg = host(dc)
+        gd = np.stack([row_parts(cg, layout, ps, q)[0] for q in slots])
+        gs = np.stack([row_parts(cg, layout, ps, q)[1] for q in slots])
+        od = np.stack([row_parts(hc, layout, ps, q)[0] for q in slots])
+        os_ = np.stack([row_parts(hc, layout, ps, q)[1] for q in slots])
+        qd, qs = oracle.store_row(layout, pre_g[idx])
+        assert np.array_equal(qd, gd) and np.array_equal(qs, gs)
+        assert_rows_close(layout, gd, gs, od, os_, spec.bf16_value(pre_o[idx]))
+        written |= set(slots)
+        pos = pos + rng.integers(0, D + 1, size=S).astype(np.int32)
+    m = written_mask(hc.shape, layout, ps, written)
+    assert np.array_equal(host(dc)[~m], hc[~m])
+
+
+# ================================================================= DCP
+@pytest.mark.parametrize("layout", ["V41", "V41_FP4"])
+def test_dcp_prefill_owner_predicate(K, layout):
+    """prefill rows dealt over 3 ranks in runs of 2; each rank's call stores
+    its own rows at its own page-table slots."""
+    world, K_, ps = 3, 2, 8
+    lengths, P = [37, 0, 120, 9, 64], [0, 0, 5, 2, 31]
+    case = W.compress_case(230, lengths, start_pos=P, ratio=2, page_size=ps, fused=True, gap=2)
+    tables, npg = W.per_rank_page_tables(231, world, len(lengths), case["page_table"].shape[1])
+    for rank in range(world):
+        _say("dcp prefill", layout, rank)
+        c = dict(case, page_table=tables[rank], num_pages=npg)
+        r = run_compress(K, c, layout, 2, oracle.PREFILL, page_table=tables[rank],
+                         dcp_world=world, dcp_rank=rank, dcp_interleave=K_)
+        lat, slots, L = [], [], 0
+        for b, (n, p0) in enumerate(zip(lengths, P)):
+            for q in range(p0, p0 + n):
+                if q % 2 == 1:
+                    ow, u = oracle.dcp_owner(q // 2, world, K_)
+                    slots.append(int(tables[rank][b, u // ps]) * ps + u % ps if ow == rank else 0)
+                    lat.append(L)
+                    L += 1
+        assert r["n_rows"] == L
+        check_compress(r, layout, ps, slots, lat)
+
+
+def test_dcp_verify_owner_predicate(K):
+    """verify through the page table under 2 ranks, runs of 4."""
+    case = W.verify_case(232, 64, draft_len=4, ratio=2, page_size=16, max_pos=512, ring_slots=3)
+    for rank in range(2):
+        _say("dcp verify", rank)
+        r = run_compress(K, case, "V41", 2, oracle.VERIFY, page_table=case["page_table"],
+                         draft_len=4, ring_slots=3, dcp_world=2, dcp_rank=rank,
+                         dcp_interleave=4)
+        lat, slots = _token_rows(case, 2, world=2, rank=rank, interleave=4)
+        check_compress(r, "V41", 16, slots, lat)
+
+
+def _filter(K, c, world, rank, interleave, k=None, valid=True):
+    ids = c["ids"] if k is None else c["ids"][:, :k]
+    T, kk = ids.shape
+    bt = c["block_tables"][rank]
+    want = oracle.dcp_filter_ids(ids, c["token_to_req"], bt, page_size=c["page_size"],
+                                 num_pages=c["num_pages"], world=world, rank=rank,
+                                 interleave=interleave, valid=c["valid"] if valid else None)
+    out = torch.full((T, kk), 12345, dtype=torch.int32, device="cuda")
+    lens = torch.full((T,), -7, dtype=torch.int32, device="cuda")
+    s = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvc_dcp_filter_ids(dev(ids), dev(c["token_to_req"]), dev(bt), out, lens,
+                         page_size=c["page_size"], num_pages=c["num_pages"], world=world,
+                         rank=rank, interleave=interleave,
+                         valid=dev(c["valid"]) if valid else None, status=s)
+    torch.cuda.synchronize()
+    return want, (host(out), host(lens), int(s.item()))
+
+
+@pytest.mark.parametrize("world,interleave,k", [(1, 1, 64), (2, 1, 100), (4, 4, 2048),
+                                                 (3, 2, 7), (8, 16, 513)])
+def test_dcp_filter_ids(K, world, interleave, k):
+    _say("dcp filter", world, interleave, k)
+    c = W.dcp_ids_case(240 + world, T=300, k=k, n_req=7, max_rows=3000, world=world,
+                       page_size=64)
+    total = 0
+    for rank in range(world):
+        (ws, wl, wst), (gs, gl, gst) = _filter(K, c, world, rank, interleave)
+        assert np.array_equal(gl, wl) and np.array_equal(gs, ws) and gst == wst
+        total += int(gl.sum())
+    assert total == int(((c["ids"] >= 0) & (c["valid"][:, None] != 0)).sum())
+
+
+def test_dcp_filter_edges(K):
+    """no valid flags, an empty id row width, requests outside the table,
+    pages outside the cache and past the table row."""
+    _say("dcp filter edges")
+    c = W.dcp_ids_case(250, T=70, k=130, n_req=4, max_rows=900, world=2, page_size=16)
+    c["token_to_req"][::9] = 9                     # no such request
+    c["block_tables"][1][1, 3] = c["num_pages"] + 5
+    c["block_tables"][1][2, 0] = -3
+    (ws, wl, wst), (gs, gl, gst) = _filter(K, c, 2, 1, 1, valid=False)
+    assert np.array_equal(gl, wl) and np.array_equal(gs, ws) and gst == wst
+    assert wst & oracle.ST_REQ_RANGE and wst & oracle.ST_PAGE_RANGE
+    (ws, wl, wst), (gs, gl, gst) = _filter(K, c, 2, 0, 2, k=0)
+    assert gs.shape[1] == 0 and np.all(gl == 0)
+
+
+# ================================================================= RoPE store
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_rope_store_bit_exact(K, layout):
+    """every byte equals the oracle's: rows of random lengths, positions
+    across a 4096-entry table, padded rows and positions outside it."""
+    _say("rope store", layout)
+    c = W.rope_store_case(260, [700, 1, 129, 64], page_size=64, max_pos=4096, pad_frac=0.05,
+                          bad_pos_frac=0.05)
+    rb = oracle.layout_bytes(layout)[2]
+    hc = np.full((c["num_pages"], 64 * rb), 0x5C, np.uint8)
+    dc = dev(hc)
+    _, st = oracle.store_rows_rope(hc, layout, 64, c["rows"], c["positions"], c["freqs"],
+                                   c["out_loc"])
+    s = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvc_store_rows_rope(K.Cache(dc, layout, 64), dev(c["rows"]), dev(c["positions"]),
+                          dev(c["freqs"]), dev(c["out_loc"]), status=s)
+    torch.cuda.synchronize()
+    assert int(s.item()) == st == oracle.ST_POS_RANGE
+    assert np.array_equal(host(dc), hc)
+
+
+def test_rope_store_c2_size(K):
+    """the ratio-1 store workload (8 requests, 512..4096 rows each) with a
+    rotary position per row, V41_FP4: bit-exact."""
+    _say("rope store C2 size")
+    c2 = W.workload_c2()
+    rng = np.random.default_rng(261)
+    pos = rng.integers(0, 16384, size=c2["rows"].shape[0]).astype(np.int32)
+    fr = W.rope_freqs(16384)
+    rb = 288
+    hc = np.zeros((c2["num_pages"], 64 * rb), np.uint8)
+    dc = dev(hc)
+    _, st = oracle.store_rows_rope(hc, "V41_FP4", 64, c2["rows"], pos, fr, c2["out_loc"])
+    K.kvc_store_rows_rope(K.Cache(dc, "V41_FP4", 64), dev(c2["rows"]), dev(pos), dev(fr),
+                          dev(c2["out_loc"]))
+    torch.cuda.synchronize()
+    assert st == 0 and np.array_equal(host(dc), hc)
+
+
+# ================================================================= graph capture
+def test_prefill_compress_graph_replay(K):
+    """The prefill compressor captured once in a graph, its offsets, start
+    positions, pending state and projection rows refreshed in place between
+    replays: every replay equals an eager call on the same inputs
+    (bit-exact) and the oracle (tolerance)."""
+    layout, ps, S, T = "V41_FP4", 16, 8, 600
+    cases = [W.compress_case(270 + i, W.ragged_lengths(np.random.default_rng(280 + i), T - 40, S),
+                             start_pos=np.random.default_rng(290 + i).integers(0, 50, size=S),
+                             ratio=2, page_size=ps, fused=True, pt_slack=3) for i in range(3)]
+    rb = oracle.layout_bytes(layout)[2]
+    npg = max(c["num_pages"] for c in cases)
+    pts = max(c["page_table"].shape[1] for c in cases)
+    max_rows = T // 2 + S
+
+    proj = torch.zeros((T, 1024), dtype=torch.int16, device="cuda")
+    offs = torch.zeros((2, S), dtype=torch.int32, device="cuda")
+    start = torch.zeros(S, dtype=torch.int32, device="cuda")
+    pt = torch.zeros((S, pts), dtype=torch.int32, device="cuda")
+    state = torch.zeros((S, 2, 512), dtype=torch.int16, device="cuda")
+    cache = torch.zeros((npg, ps * rb), dtype=torch.uint8, device="cuda")
+    lat = torch.zeros((max_rows, 512), dtype=torch.int16, device="cuda")
+    pre = torch.zeros_like(lat)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    w = dev(cases[0]["norm_w"])
+    fr = dev(W.rope_freqs(T + 64))
+
+    def load(c):
+        proj.zero_()
+        proj[:c["kv"].shape[0]].copy_(dev(c["kv"]))
+        offs.copy_(dev(c["offsets"]))
+        start.copy_(dev(c["start_pos"]))
+        pt.zero_()
+        pt[:, :c["page_table"].shape[1]].copy_(dev(c["page_table"]))
+        state.copy_(dev(c["state"]))
+        cache.zero_()
+        lat.zero_()
+        pre.zero_()
+
+    def call():
+        status.zero_()
+        K.kvc_compress_store(ratio=2, mode=K.MODE_PREFILL, kv=proj[:, :512], score=proj[:, 512:],
+                             start_pos=start, cache=K.Cache(cache, layout, ps), norm_w=w,
+                             eps=1e-6, freqs=fr, latent_out=lat, offsets=offs, page_table=pt,
+                             state=state, prequant_out=pre, status=status)
+
+    def snap():
+        return [host(t).copy() for t in (cache, lat, pre, state, status)]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        load(cases[0])
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, c in enumerate(cases):
+            _say("graph replay", rep, i)
+            load(c)
+            torch.cuda.synchronize()
+            call()                                   # eager on the same inputs
+            torch.cuda.synchronize()
+            eager = snap()
+            load(c)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            replay = snap()
+            for a, b in zip(eager, replay):
+                assert np.array_equal(a, b), (rep, i)
+            if rep == 0:
+                lat_o, _, st_o, n = oracle.compress(
+                    ratio=2, mode=oracle.PREFILL, kv=c["kv"], fused=True, offsets=c["offsets"],
+                    start_pos=c["start_pos"], page_table=c["page_table"],
+                    state=c["state"].copy(), norm_w=cases[0]["norm_w"], eps=1e-6,
+                    freqs=W.rope_freqs(T + 64), cache=np.zeros((c["num_pages"], ps * rb), np.uint8),
+                    layout=layout, page_size=ps)
+                assert st_o == 0 and int(replay[4][0]) == 0
+                assert_latent_close(replay[1].view(np.uint16)[:n], lat_o)

@@ -12,8 +12,8 @@ import torch
 import oracle
 import workloads as W
 from tests import spec
-from tests.gpu_util import (assert_latent_close, assert_rows_close, dev, host, row_parts, sha,
-                            written_mask)
+from tests.gpu_util import (assert_latent_close, assert_rows_close, check_compress, dev, host,
+                            row_parts, run_compress, sha, written_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -209,77 +209,8 @@ def test_gather_reuse_head(K):
 
 
 # ===================================================================== compress
-def _run_compress(K, case, layout, ratio, mode, fused=True, eps=None, max_out_rows=None,
-                  out_loc=None, page_table="case", want_state=True, cache_fill=0xA5):
-    """run oracle and GPU on the same inputs; returns dict of both sides."""
-    ps = case["page_size"]
-    db, sb, rb, _ = oracle.layout_bytes(layout)
-    eps = case["eps"] if eps is None else eps
-    hc = np.full((case["num_pages"], ps * rb), cache_fill, np.uint8)
-    dc = dev(hc)
-    state_h = case["state"].copy()
-    state_d = dev(case["state"])
-    pt = case["page_table"] if isinstance(page_table, str) else page_table
-    start = case["start_pos"] if mode == oracle.PREFILL else case["pos"]
-    kv = case["kv"]
-    if fused:
-        o_kw = dict(kv=kv, fused=True)
-    else:
-        o_kw = dict(kv=kv, score=case["score"], fused=False)
-    lat_o, pre_o, st_o, n_rows = oracle.compress(
-        ratio=ratio, mode=mode, offsets=case.get("offsets"), start_pos=start, page_table=pt,
-        out_loc=out_loc, state=state_h, norm_w=case["norm_w"], eps=eps, freqs=case["freqs"],
-        cache=hc, layout=layout, page_size=ps, max_out_rows=max_out_rows, **o_kw)
-    nlat = lat_o.shape[0]
-    lat = torch.zeros((max(nlat, 1), 512), dtype=torch.int16, device="cuda")
-    pre = torch.zeros_like(lat)
-    kvd = dev(kv)
-    if fused:
-        kv_v, sc_v = kvd[:, :512], kvd[:, 512:]
-    else:
-        kv_v = kvd
-        sc_v = dev(case["score"]) if case["score"] is not None else None
-    s = _status()
-    K.kvc_compress_store(
-        ratio=ratio, mode=mode, kv=kv_v, score=sc_v if ratio == 2 else None,
-        start_pos=dev(start), cache=K.Cache(dc, layout, ps), norm_w=dev(case["norm_w"]), eps=eps,
-        freqs=dev(case["freqs"]), latent_out=lat, max_out_rows=nlat,
-        offsets=None if case.get("offsets") is None or mode == oracle.DECODE else dev(case["offsets"]),
-        page_table=None if pt is None else dev(pt),
-        out_loc=None if out_loc is None else dev(out_loc),
-        state=state_d if ratio == 2 else None, prequant_out=pre, status=s)
-    torch.cuda.synchronize()
-    return dict(lat_o=lat_o, pre_o=pre_o, st_o=st_o, n_rows=n_rows, cache_o=hc, state_o=state_h,
-                lat_g=host(lat, np.uint16)[:nlat], pre_g=host(pre, np.uint16)[:nlat],
-                st_g=int(s.item()), cache_g=host(dc), state_g=host(state_d, np.uint16),
-                cache_fill=cache_fill)
-
-
-def _check_compress(r, layout, ps, touched_slots, emitted):
-    """emitted: latent indices that carry rows; touched_slots: their slots
-    (0 = none), same order."""
-    assert r["st_g"] == r["st_o"], (r["st_g"], r["st_o"])
-    em = np.asarray(emitted, np.int64)
-    if em.size:
-        assert_latent_close(r["lat_g"][em], r["lat_o"][em])
-        assert_latent_close(r["pre_g"][em], r["pre_o"][em], "prequant")
-    # untouched cache bytes identical (sentinel)
-    slots = [s for s in touched_slots if s != 0]
-    m = written_mask(r["cache_g"].shape, layout, ps, slots)
-    assert np.array_equal(r["cache_g"][~m], r["cache_o"][~m])
-    # the kernel's quantizer is bit-exact given its own pre-quant rows,
-    # and the fused rows are within one code step of the oracle's
-    idx = [i for i, s in zip(emitted, touched_slots) if s != 0]
-    if idx:
-        gd = np.stack([row_parts(r["cache_g"], layout, ps, s)[0] for s in slots])
-        gs = np.stack([row_parts(r["cache_g"], layout, ps, s)[1] for s in slots])
-        od = np.stack([row_parts(r["cache_o"], layout, ps, s)[0] for s in slots])
-        os_ = np.stack([row_parts(r["cache_o"], layout, ps, s)[1] for s in slots])
-        qd, qs = oracle.store_row(layout, r["pre_g"][idx])
-        assert np.array_equal(qd, gd) and np.array_equal(qs, gs), "quantizer not bit-exact"
-        assert_rows_close(layout, gd, gs, od, os_, spec.bf16_value(r["pre_o"][idx]))
-    # pending state: an exact copy
-    assert np.array_equal(r["state_g"], r["state_o"])
+_run_compress = run_compress
+_check_compress = check_compress
 
 
 def _prefill_slots(case, ratio):
