@@ -52,12 +52,166 @@ def measured_traffic(kernel: str):
     return e.get("bytes_per_launch")
 
 
+def _time_events(fn, stream, reps: int, warmup: int = 3):
+    """mean device time in seconds of one fn() call.  The calls are captured
+    back to back in a HIP graph so that host-side launch cost does not pace
+    them (small kernels run faster than Python can launch them); HIP events
+    on the replay stream bracket three replays of the graph."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(3):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (3 * reps) / 1e3
+
+
+def measure_next_rows(kvc, W, d, dev, stream):
+    """Throughput of the entry points beyond the two headline kernels, each on
+    a workload of the path's own shapes, with its algorithmic HBM bytes."""
+    import numpy as np
+    import torch
+
+    res = {}
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def entry(name, secs, nbytes, units, unit):
+        res[name] = {"us": secs * 1e6, "bytes": int(nbytes), "gbps": nbytes / secs / 1e9,
+                     "frac": nbytes / secs / 1e9 / HBM_PEAK_GBS, unit: units / secs}
+
+    # verify: 1024 slots x 4 drafts, ring of 3, V41_FP4 cache through page tables
+    vc = W.verify_case(20261206, 1024, draft_len=4, ratio=2, page_size=64, max_pos=4096,
+                       ring_slots=3)
+    fp4 = kvc.kvc_layout_query("V41_FP4")
+    S, D = vc["S"], vc["draft_len"]
+    pos = vc["pos"].astype(np.int64)
+    q = pos[:, None] + np.arange(D)[None, :]
+    rows = int((q % 2 == 1).sum())
+    pend = int((q % 2 == 0).sum())
+    first_from_ring = int((pos % 2 == 1).sum())
+    vbytes = S * D * 2048 + first_from_ring * 2048 + rows * (1024 + fp4.row_bytes) + pend * 2048
+    vp = d(vc["kv"])
+    vargs = dict(ratio=2, mode=kvc.MODE_VERIFY, kv=vp[:, :512], score=vp[:, 512:],
+                 start_pos=d(vc["pos"]), page_table=d(vc["page_table"]), state=d(vc["state"]),
+                 norm_w=d(vc["norm_w"]), eps=vc["eps"], freqs=d(vc["freqs"]),
+                 latent_out=torch.empty((S * D, 512), dtype=torch.int16, device=dev),
+                 cache=kvc.Cache(torch.zeros((vc["num_pages"], 64 * fp4.row_bytes),
+                                             dtype=torch.uint8, device=dev), "V41_FP4", 64),
+                 draft_len=D, ring_slots=3, status=status)
+    secs = _time_events(lambda: kvc.kvc_compress_store(**vargs), stream, 50)
+    entry("verify_1024x4_v41fp4", secs, vbytes, rows, "rows_per_s")
+
+    # decode: 1024 slots x 1 token, ratio 2, explicit out_loc, V4 cache
+    c5 = W.workload_c5()
+    v4 = kvc.kvc_layout_query("V4")
+    dp = d(c5["kv"])
+    dpos = c5["pos"].astype(np.int64)
+    drows = int((dpos % 2 == 1).sum())
+    dbytes = 1024 * 2048 + drows * (2048 + 1024 + v4.row_bytes) + (1024 - drows) * 2048
+    dargs = dict(ratio=2, mode=kvc.MODE_DECODE, kv=dp[:, :512], score=dp[:, 512:],
+                 start_pos=d(c5["pos"]), out_loc=d(c5["out_loc"]), state=d(c5["state"]),
+                 norm_w=d(c5["norm_w"]), eps=c5["eps"], freqs=d(c5["freqs"]),
+                 latent_out=torch.empty((1024, 512), dtype=torch.int16, device=dev),
+                 cache=kvc.Cache(torch.zeros((c5["num_pages"], 64 * v4.row_bytes),
+                                             dtype=torch.uint8, device=dev), "V4", 64),
+                 status=status)
+    secs = _time_events(lambda: kvc.kvc_compress_store(**dargs), stream, 50)
+    entry("decode_1024_v4", secs, dbytes, drows, "rows_per_s")
+
+    # RoPE store: the ratio-1 store workload (8 requests, 512..4096 rows) with
+    # a rotary position per row, into V41_FP4
+    c2 = W.workload_c2()
+    n2 = c2["rows"].shape[0]
+    rng = np.random.default_rng(20261207)
+    pos2 = d(rng.integers(0, 16384, size=n2).astype(np.int32))
+    fr2 = d(W.rope_freqs(16384))
+    rcache = kvc.Cache(torch.zeros((c2["num_pages"], 64 * fp4.row_bytes), dtype=torch.uint8,
+                                   device=dev), "V41_FP4", 64)
+    rrows, rloc = d(c2["rows"]), d(c2["out_loc"])
+    secs = _time_events(lambda: kvc.kvc_store_rows(rcache, rrows, rloc, status), stream, 50)
+    entry("store_c2_v41fp4", secs, n2 * (1024 + fp4.row_bytes + 4), n2, "rows_per_s")
+    secs = _time_events(lambda: kvc.kvc_store_rows_rope(rcache, rrows, pos2, fr2, rloc, status),
+                        stream, 50)
+    entry("rope_store_c2_v41fp4", secs, n2 * (1024 + fp4.row_bytes + 8), n2, "rows_per_s")
+
+    # DCP filter: 4096 tokens x 2048 global ids, 4 ranks, runs of 4, rank 1
+    dc = W.dcp_ids_case(20261208, T=4096, k=2048, n_req=32, max_rows=65536, world=4,
+                        page_size=64)
+    T, k = dc["ids"].shape
+    f_ids, f_t2r, f_bt = d(dc["ids"]), d(dc["token_to_req"]), d(dc["block_tables"][1])
+    f_valid = d(dc["valid"])
+    f_out = torch.empty((T, k), dtype=torch.int32, device=dev)
+    f_lens = torch.empty(T, dtype=torch.int32, device=dev)
+    secs = _time_events(lambda: kvc.kvc_dcp_filter_ids(
+        f_ids, f_t2r, f_bt, f_out, f_lens, page_size=64, num_pages=dc["num_pages"], world=4,
+        rank=1, interleave=4, valid=f_valid, status=status), stream, 50)
+    entry("dcp_filter_4096x2048_w4", secs, T * k * 8 + T * 12, T * k, "ids_per_s")
+
+    # graph replay vs eager launch of the small prefill compress (one 64-token
+    # request, ratio 2, V41): host wall time per call, back to back
+    c1 = W.workload_c1()
+    v41 = kvc.kvc_layout_query("V41")
+    c1args = dict(ratio=2, mode=kvc.MODE_PREFILL, kv=d(c1["kv"]), score=d(c1["score"]),
+                  start_pos=d(c1["start_pos"]), offsets=d(c1["offsets"]),
+                  page_table=d(c1["page_table"]), state=d(c1["state"]), norm_w=d(c1["norm_w"]),
+                  eps=c1["eps"], freqs=d(c1["freqs"]),
+                  latent_out=torch.empty((32, 512), dtype=torch.int16, device=dev),
+                  cache=kvc.Cache(torch.zeros((c1["num_pages"], 64 * v41.row_bytes),
+                                              dtype=torch.uint8, device=dev), "V41", 64))
+    n_calls = 2000
+    for _ in range(10):
+        kvc.kvc_compress_store(**c1args)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(n_calls):
+        kvc.kvc_compress_store(**c1args)
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t) / n_calls
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kvc.kvc_compress_store(**c1args)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(20):
+            kvc.kvc_compress_store(**c1args)
+    g.replay()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(n_calls // 20):
+        g.replay()
+    torch.cuda.synchronize()
+    replay = (time.perf_counter() - t) / n_calls
+    res["graph_c1_compress"] = {"eager_us_per_call": eager * 1e6,
+                                "graph_us_per_call": replay * 1e6,
+                                "calls_per_graph": 20, "calls": n_calls}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the verify / RoPE-store / DCP-filter / graph-replay measurements")
     ap.add_argument("--gather-blocks", type=int, default=0)
     ap.add_argument("--compress-blocks", type=int, default=0)
     ap.add_argument("--compress-tile-rows", type=int, default=0)
@@ -123,31 +277,46 @@ def main() -> int:
 
     stream = torch.cuda.current_stream()
 
-    def step(k, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def compress():
         kvc.kvc_compress_store(**c3_args, status=status)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def gather(k):
         kvc.kvc_dequant_gather(g_cache, g_pt, g_ids, g_outs[k % 3], status)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def step(k):
+        compress()
+        gather(k)
 
     # ---------------------------------------------------------------- timing
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
     assert int(status.item()) == 0, f"device status {int(status.item())}"
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
-        step(k, events[k])
+        step(k)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    comp_ms = [e[0].elapsed_time(e[1]) for e in events]
-    gath_ms = [e[1].elapsed_time(e[2]) for e in events]
     ms_step = elapsed * 1e3 / args.steps
+
+    # per-kernel durations: HIP events on the launch stream around runs of
+    # back-to-back launches of one kernel (an event between every two kernels
+    # would add its own gap to each interval)
+    runs = max(args.steps // 10, 2)
+    comp_ms, gath_ms = [], []
+    for r in range(runs):
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        for _ in range(10):
+            compress()
+        b.record(stream)
+        for k in range(10):
+            gather(k)
+        c.record(stream)
+        torch.cuda.synchronize()
+        comp_ms.append(a.elapsed_time(b) / 10)
+        gath_ms.append(b.elapsed_time(c) / 10)
 
     comp_bytes = c3_rows * (4096 + 1024 + fp4.row_bytes) + c3_tails * 2 * 2048
     gath_bytes = n_ids * (v41.row_bytes + 1024 + 4)
@@ -185,10 +354,12 @@ def main() -> int:
         "hbm_gbps": (comp_bytes + gath_bytes) / (ms_step / 1e3) / 1e9,
         "kernels": {
             "compress_store": {"us": float(np.mean(comp_ms)) * 1e3, "p90_us": float(np.percentile(comp_ms, 90)) * 1e3,
+                               "launches_timed": 10 * runs,
                                "bytes": comp_bytes, "gbps": comp_gbs, "frac": comp_gbs / HBM_PEAK_GBS,
                                "rows_per_s": c3_rows / comp_s,
                                "traffic": measured_traffic("compress_store")},
             "dequant_gather": {"us": float(np.mean(gath_ms)) * 1e3, "p90_us": float(np.percentile(gath_ms, 90)) * 1e3,
+                               "launches_timed": 10 * runs,
                                "bytes": gath_bytes, "gbps": gath_gbs, "frac": gath_gbs / HBM_PEAK_GBS,
                                "rows_per_s": n_ids / gath_s},
         },
@@ -197,6 +368,9 @@ def main() -> int:
                      "kernel": "dequant_gather", "algorithmic_bytes": gath_bytes},
         "cpu_baseline": None,
     }
+
+    if not args.no_next_rows:
+        out["next_rows"] = measure_next_rows(kvc, W, d, dev, stream)
 
     # ---------------------------------------------------------------- oracle
     if not args.no_cpu_baseline:

@@ -462,23 +462,36 @@ __global__ __launch_bounds__(kBlock) void compress_tokens_kernel(CompressParams 
   const uint4 wr = ld_u4(p.norm_w + kDimsPerLane * lane);
   const float w[8] = {bf16_lo(wr.x), bf16_hi(wr.x), bf16_lo(wr.y), bf16_hi(wr.y),
                       bf16_lo(wr.z), bf16_hi(wr.z), bf16_lo(wr.w), bf16_hi(wr.w)};
-  for (int32_t jj = 0; jj < D; ++jj) {
+  // the slot's rows two at a time, the loads of both issued before either
+  // is finished (a lone last row loads its inputs twice)
+  auto job = [&](int32_t jj) {
     const int64_t q = P + jj;
-    if (RATIO == 2 && (q & 1) == 0) continue;    // first token of a pair: pending
-    RowJob j;
-    j.t1 = t0 + jj;
-    j.latent_idx = t0 + jj;
-    j.from_state = RATIO == 2 && jj == 0;
-    j.st_row = j.from_state ? ring_row(p, b, q >> 1) : 0;
-    j.rot_pos = RATIO == 2 ? q - 1 : q;
+    RowJob r;
+    r.t1 = t0 + jj;
+    r.latent_idx = t0 + jj;
+    r.from_state = RATIO == 2 && jj == 0;
+    r.st_row = r.from_state ? ring_row(p, b, q >> 1) : 0;
+    r.rot_pos = RATIO == 2 ? q - 1 : q;
     // destination: the caller's out_loc (0 = padded row) or the page table
     if (p.out_loc != nullptr) {
-      j.loc = ld_ro(p.out_loc + t0 + jj);
-      j.loc_err = 0;
+      r.loc = ld_ro(p.out_loc + t0 + jj);
+      r.loc_err = 0;
     } else {
-      dest_loc(p, b, RATIO == 2 ? (q >> 1) : q, j.loc, j.loc_err);
+      dest_loc(p, b, RATIO == 2 ? (q >> 1) : q, r.loc, r.loc_err);
     }
-    finish_row<L, RATIO>(p, kv, w, j, load_row<RATIO>(p, j));
+    return r;
+  };
+  // tokens that close a row: every token (ratio 1), odd positions (ratio 2)
+  const int32_t first = (RATIO == 2 && (P & 1) == 0) ? 1 : 0;
+  const int32_t step = RATIO == 2 ? 2 : 1;
+  for (int32_t jj = first; jj < D; jj += 2 * step) {
+    const bool two = jj + step < D;
+    const RowJob j0 = job(jj);
+    const RowJob j1 = two ? job(jj + step) : j0;
+    const RowIn in0 = load_row<RATIO>(p, j0);
+    const RowIn in1 = load_row<RATIO>(p, j1);
+    finish_row<L, RATIO>(p, kv, w, j0, in0);
+    if (two) finish_row<L, RATIO>(p, kv, w, j1, in1);
   }
   if constexpr (RATIO == 2) {
     // an even position's token becomes the pending token of its pair, unless

@@ -26,92 +26,148 @@ __device__ __forceinline__ void raise_status(int32_t* status, int32_t bit) {
 }
 
 // ------------------------------------------------------------------ store
+// A wave stores kStoreRows rows per loop trip: the loads of all of them (row
+// bytes, destination, position) are issued before the first is quantized, so
+// a wave keeps 4 KiB of reads in flight.  Rows past n reload row n - 1 (a
+// fixed count of loads keeps the compiler's waits exact) and store nothing.
 // ROPE: rotate the rope dims at positions[i] first (exact, one rounding).
+constexpr int kStoreRows = 4;
+
 template <int L, bool ROPE>
 __global__ __launch_bounds__(kBlock) void store_rows_kernel(StoreParams p) {
   const PagedKV<L> kv = paged<L>(p.cache);
   const int lane = lane_id();
   const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t i = wave0; i < p.n; i += nwaves) {
-    uint4 x = ld_u4_nt(p.rows + i * p.row_stride + kDimsPerLane * lane);
-    const int64_t loc = uniform(p.out_loc[i]);
-    bool write = loc != 0;
-    if constexpr (ROPE) {
-      if (write) {
-        const int64_t pos = ld_ro(p.positions + i);
-        if (pos < 0 || pos >= p.max_pos) {
-          raise_status(p.status, kStPosRange);
-          write = false;
-        } else {
-          x = rope_row_exact(x, p.freqs + pos * kRope);
+  for (int64_t i0 = wave0 * kStoreRows; i0 < p.n; i0 += nwaves * kStoreRows) {
+    uint4 x[kStoreRows];
+    int64_t loc[kStoreRows], pos[kStoreRows];
+#pragma unroll
+    for (int u = 0; u < kStoreRows; ++u) {
+      const int64_t i = i0 + u < p.n ? i0 + u : p.n - 1;
+      x[u] = ld_u4_nt(p.rows + i * p.row_stride + kDimsPerLane * lane);
+      loc[u] = ld_ro(p.out_loc + i);
+      pos[u] = ROPE ? ld_ro(p.positions + i) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kStoreRows; ++u) {
+      if (i0 + u >= p.n) break;
+      bool write = loc[u] != 0;
+      if constexpr (ROPE) {
+        if (write) {
+          if (pos[u] < 0 || pos[u] >= p.max_pos) {
+            raise_status(p.status, kStPosRange);
+            write = false;
+          } else {
+            x[u] = rope_row_exact(x[u], p.freqs + pos[u] * kRope);
+          }
         }
       }
+      if (write && !kv.valid(loc[u])) {
+        raise_status(p.status, kStPageRange);
+        write = false;
+      }
+      const int64_t slot = write ? loc[u] : 0;
+      store_row_wave<L>(x[u], kv.data(slot), kv.scale(slot), write);
     }
-    if (write && !kv.valid(loc)) {
-      raise_status(p.status, kStPageRange);
-      write = false;
-    }
-    const int64_t slot = write ? loc : 0;
-    store_row_wave<L>(x, kv.data(slot), kv.scale(slot), write);
   }
 }
 
 // ------------------------------------------------------------------ DCP ids
-// One wave per row of ids, 64 ids per step: each lane tests its id for
-// ownership and maps it to a slot, a ballot and a lane count give every kept
-// id its place after the ones before it, and the row is finished with -1.
+// One workgroup per row of ids, kFilterPerLane consecutive ids per lane
+// (2048 ids per pass): every lane tests its ids for ownership and looks up
+// their pages (all loads in flight together), the workgroup scans the lanes'
+// kept counts (shuffles within a wave, LDS across the four waves),
+// and each lane writes its kept slots at its offset; the row ends in -1.
+constexpr int kFilterPerLane = 8;
+constexpr int kFilterPass = kBlock * kFilterPerLane;
+
 __global__ __launch_bounds__(kBlock) void dcp_filter_kernel(DcpFilterParams p) {
-  const int lane = lane_id();
-  const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  __shared__ int32_t wave_cnt[kWavesPerBlock];
+  const int lane = lane_id(), wid = threadIdx.x >> 6;
   const int kl = p.interleave_log2;
   const uint32_t kmask = (1u << kl) - 1, pmask = (1u << p.page_bits) - 1;
   const uint32_t world = (uint32_t)p.world, rank = (uint32_t)p.rank;
-  for (int64_t t = wave0; t < p.T; t += nwaves) {
-    int32_t cnt = 0;
+  for (int64_t t = blockIdx.x; t < p.T; t += gridDim.x) {
     bool keep = p.valid == nullptr || ld_ro(p.valid + t) != 0;
     const int32_t req = ld_ro(p.token_to_req + t);
     if (keep && (req < 0 || req >= p.n_req)) {
-      raise_status(p.status, kStReqRange);
+      if (threadIdx.x == 0 && p.status != nullptr) atomicOr(p.status, kStReqRange);
       keep = false;
     }
     int32_t* out = p.out_slots + t * p.out_stride;
+    int32_t cnt = 0;                                   // kept so far (workgroup-uniform)
     if (keep) {
       const int32_t* row = p.ids + t * p.ids_stride;
       const int32_t* bt = p.block_table + (int64_t)req * p.bt_stride;
-      for (int32_t i0 = 0; i0 < p.k; i0 += kLanes) {
-        const int32_t i = i0 + lane;
-        int32_t slot = -1, bad = 0;
-        const int32_t id = i < p.k ? row[i] : -1;
-        if (id >= 0) {
-          const uint32_t run = (uint32_t)id >> kl;
-          const uint32_t turn = run / world;
-          if (run - turn * world == rank) {
-            const uint32_t u = (turn << kl) | ((uint32_t)id & kmask);
-            const int64_t lp = u >> p.page_bits;
-            if (lp >= p.bt_stride) {
-              bad = kStPtRange;
+      for (int32_t s0 = 0; s0 < p.k; s0 += kFilterPass) {
+        const int32_t base = s0 + (int32_t)threadIdx.x * kFilterPerLane;
+        int32_t id[kFilterPerLane], lp[kFilterPerLane], u[kFilterPerLane], pg[kFilterPerLane];
+#pragma unroll
+        for (int e = 0; e < kFilterPerLane; ++e) {
+          const int32_t i = base + e;
+          const int32_t v = row[i < p.k ? i : p.k - 1];
+          id[e] = i < p.k ? v : -1;
+        }
+        // ownership and the page-table entry to read (entry 0 when unused)
+#pragma unroll
+        for (int e = 0; e < kFilterPerLane; ++e) {
+          lp[e] = -1;
+          u[e] = 0;
+          if (id[e] >= 0) {
+            const uint32_t run = (uint32_t)id[e] >> kl;
+            const uint32_t turn = run / world;
+            if (run - turn * world == rank) {
+              u[e] = (int32_t)((turn << kl) | ((uint32_t)id[e] & kmask));
+              lp[e] = u[e] >> p.page_bits;
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < kFilterPerLane; ++e) pg[e] = bt[lp[e] >= 0 && lp[e] < p.bt_stride ? lp[e] : 0];
+        int32_t slot[kFilterPerLane], n = 0, bad = 0;
+#pragma unroll
+        for (int e = 0; e < kFilterPerLane; ++e) {
+          slot[e] = -1;
+          if (lp[e] >= 0) {
+            if (lp[e] >= p.bt_stride) {
+              bad |= kStPtRange;
+            } else if (pg[e] < 0 || pg[e] >= p.num_pages) {
+              bad |= kStPageRange;
             } else {
-              const int32_t phys = bt[lp];
-              if (phys < 0 || phys >= p.num_pages) {
-                bad = kStPageRange;
-              } else {
-                slot = (phys << p.page_bits) | (int32_t)(u & pmask);
-              }
+              slot[e] = (pg[e] << p.page_bits) | (int32_t)((uint32_t)u[e] & pmask);
+              ++n;
             }
           }
         }
         if (bad != 0 && p.status != nullptr) atomicOr(p.status, bad);
-        const uint64_t m = __ballot(slot >= 0);
-        const int32_t before = (int32_t)__builtin_amdgcn_mbcnt_hi(
-            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        if (slot >= 0) out[cnt + before] = slot;
-        cnt += (int32_t)__builtin_popcountll(m);
+        // exclusive offset of this lane's kept ids within the pass
+        int32_t inc = n;
+#pragma unroll
+        for (int d = 1; d < kLanes; d <<= 1) {
+          const int32_t v = __shfl_up(inc, d);
+          if (lane >= d) inc += v;
+        }
+        if (lane == kLanes - 1) wave_cnt[wid] = inc;
+        __syncthreads();
+        int32_t before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+          const int32_t c = wave_cnt[w];
+          before += w < wid ? c : 0;
+          total += c;
+        }
+        int32_t o = cnt + before + inc - n;
+#pragma unroll
+        for (int e = 0; e < kFilterPerLane; ++e) {
+          if (slot[e] >= 0) out[o++] = slot[e];
+        }
+        cnt += total;
+        __syncthreads();                                 // wave_cnt is reused
       }
     }
-    for (int32_t i = cnt + lane; i < p.k; i += kLanes) out[i] = -1;
-    if (lane == 0) p.out_lens[t] = cnt;
+    for (int32_t i = cnt + (int32_t)threadIdx.x; i < p.k; i += kBlock) out[i] = -1;
+    if (threadIdx.x == 0) p.out_lens[t] = cnt;
   }
 }
 
@@ -258,7 +314,7 @@ LaunchTuning& launch_tuning() {
 }
 
 hipError_t launch_store_rows(const StoreParams& p, hipStream_t stream) {
-  const int blocks = grid_for(p.n, kWavesPerBlock, 8192);
+  const int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * kStoreRows, 8192);
   const bool rope = p.positions != nullptr;
   switch (p.cache.layout) {
     case kV41:
@@ -274,7 +330,7 @@ hipError_t launch_store_rows(const StoreParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_dcp_filter(const DcpFilterParams& p, hipStream_t stream) {
-  return launch(dcp_filter_kernel, grid_for(p.T, kWavesPerBlock, 4096), p, stream);
+  return launch(dcp_filter_kernel, grid_for(p.T, 1, 16384), p, stream);
 }
 
 hipError_t launch_dequant_gather(const GatherParams& p, hipStream_t stream) {
