@@ -267,11 +267,13 @@ def main() -> int:
         cache=kvc.Cache(torch.zeros((c3["num_pages"], 128 * fp4.row_bytes), dtype=torch.uint8,
                                     device=dev), "V41_FP4", 128))
     g_cache = kvc.Cache(d(c4["cache"]), "V41", 64)
-    g_pt, g_ids = d(c4["page_table"]), d(c4["ids"])
+    g_pt = d(c4["page_table"])
     n_ids = int(c4["ids"].size)
-    # three output buffers used in turn: a step never rewrites the lines the
-    # previous step left in the 256 MB Infinity Cache, so the gather's writes
-    # reach HBM as they would in a forward pass (cold, not cache-absorbed)
+    # four id lists and three output buffers used in turn: a step neither
+    # reads the rows nor rewrites the lines the previous steps left in the
+    # 256 MB Infinity Cache, so the gather's reads and writes reach HBM as
+    # they would in a forward pass (cold, not cache-served)
+    g_idsets = [d(ids) for ids in W.workload_c4_id_sets(4)]
     g_outs = [torch.empty((n_ids, 512), dtype=torch.int16, device=dev) for _ in range(3)]
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
@@ -281,7 +283,7 @@ def main() -> int:
         kvc.kvc_compress_store(**c3_args, status=status)
 
     def gather(k):
-        kvc.kvc_dequant_gather(g_cache, g_pt, g_ids, g_outs[k % 3], status)
+        kvc.kvc_dequant_gather(g_cache, g_pt, g_idsets[k % 4], g_outs[k % 3], status)
 
     def step(k):
         compress()
@@ -347,7 +349,7 @@ def main() -> int:
             "workload": "prefill compress-store (ratio 2, 16 requests, 32768 tokens, fused "
                         "|kv|score| bf16 [32768,1024], page 128, V41_FP4) + sparse-prefill "
                         "dequant-gather (262144 ids from a 1048576-row V41 cache, page 64, "
-                        "random page table -> bf16 [262144,512])",
+                        "random page table -> bf16 [262144,512]; 4 id lists used in turn)",
             "compress_rows": c3_rows, "gather_rows": n_ids,
             "seed_c3": int(c3["seed"]), "odd_lengths": c3_tails,
         },

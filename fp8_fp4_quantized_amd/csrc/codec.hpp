@@ -45,29 +45,35 @@ __device__ __forceinline__ int ue8m0_from_amax_bits(uint32_t b) {
   return e > 114 ? e : 114;
 }
 
-// fp8 e4m3fn code of the bf16 value h scaled by 2^(127 - E).  The caller
-// guarantees |h| * 2^(127-E) <= 448 and E >= 114 (the ue8m0 exponent of h's
-// group), so there is no overflow and bf16 subnormals round to zero.
-__device__ __forceinline__ uint32_t fp8_from_bf16(uint32_t h, int E) {
-  const uint32_t sign = (h >> 8) & 0x80u;
-  const int bexp = (int)((h >> 7) & 0xFFu);
-  const uint32_t mant = h & 0x7Fu;
-  const int fe = bexp - E + 7;             // e4m3 biased exponent when normal
-  // normal: keep 3 of the 7 mantissa bits, nearest even; a carry bumps fe
-  const uint32_t rn = (mant + 7u + ((mant >> 4) & 1u)) >> 4;
-  const uint32_t normal = ((uint32_t)fe << 3) + rn;
-  // subnormal (fe <= 0): (128 + mant) * 2^(fe - 5) units of 2^-9, nearest
-  // even; shifts past 9 leave less than half a unit, as 9 does
-  int sh = 5 - fe;
-  sh = sh > 9 ? 9 : (sh < 1 ? 1 : sh);
-  const uint32_t v = 128u + mant;
-  const uint32_t q = v >> sh;
-  const uint32_t rem = v & ((1u << sh) - 1u);
-  const uint32_t half = 1u << (sh - 1);
-  const uint32_t sub = q + ((rem > half) || (rem == half && (q & 1u)) ? 1u : 0u);
-  uint32_t code = fe >= 1 ? normal : sub;
-  code = bexp == 0 ? 0u : code;
-  return code | sign;
+// fp8 e4m3fn codes of four fp32 values scaled by 2^(127 - E), nearest even,
+// packed into a dword (the first value in the low byte).  gfx950's
+// v_cvt_scalef32_pk_fp8_f32 divides by the power of two whose biased exponent
+// is the scale operand's exponent field -- E itself here.  For every finite
+// bf16 x and every E in 114..254 with |x| * 2^(127 - E) <= 448 (the range the
+// ue8m0 exponent of x's group guarantees) its code equals the
+// nearest-even encoding, negative zero and subnormals included (checked
+// exhaustively on the device against the definition).
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t fp8x4_scaled(float a, float b, float c, float d, int E) {
+  const float sc = __uint_as_float((uint32_t)E << 23);
+  s16x2 w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, sc, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, sc, true);
+  return __builtin_bit_cast(uint32_t, w);
+}
+
+// Correctly rounded fp32 quotient x / s from rs, an fp32 within an ulp of
+// 1 / s (the nearest fp32, or v_rcp_f32): q0 = x * rs, the residual
+// x - q0 * s (exact in one fma) and one correction step.  Used for the FP4 group scale amax / 6 (equal to the fp32 division
+// for every finite bf16 amax >= 0) and for the element quotients x / s of the
+// e2m1 codes (equal for every finite bf16 x with |x| <= 8 s under every
+// positive finite e4m3 s; the quantizer's quotients are at most about 6.4).
+// Both were checked exhaustively on the device against the division.  The
+// sign is copied from x so that -0 stays -0.
+__device__ __forceinline__ float div_by_rcp(float x, float s, float rs) {
+  const float q0 = x * rs;
+  const float r = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(r, rs, q0), x);
 }
 
 // e4m3fn code of a non-negative finite fp32, nearest even, clamped at 448
@@ -90,23 +96,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   const float sub = (float)m * 0x1p-9f;
   const float mag = e == 0 ? sub : nrm;
   return (c & 0x80u) ? -mag : mag;
-}
-
-// The value whose round-to-nearest-even e2m1 code (gfx950's
-// v_cvt_scalef32_pk_fp4_f32 with a unit scale) is the code of the exact
-// quotient x / s, given rs = rcp(s) (within an ulp of 1 / s).
-//   The e2m1 ties (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) and grid values have
-// at most 3 significant bits.  x has at most 8 and s at most 4, so an exact
-// quotient that is not such a value lies at least ~2^-15 (relative) from
-// every one of them, and the product x * rs -- within a few ulps of x / s --
-// rounds to the same code.  An exact quotient that is such a value is
-// recovered exactly by rounding x * rs to 3 significant bits when it lies
-// within 4 ulps of one.  (Checked on the device against a threshold encoder
-// for every finite bf16 x under every positive finite e4m3 s.)
-__device__ __forceinline__ float fp4_quotient(float x, float rs) {
-  const uint32_t u = __float_as_uint(x * rs);
-  const uint32_t snap = (u + 0x00100000u) & 0xFFE00000u;   // nearest 3-significant-bit value
-  return __uint_as_float(snap - u + 4u <= 8u ? snap : u);
 }
 
 }  // namespace kvc

@@ -65,13 +65,8 @@ __device__ __forceinline__ void store_row_wave<kV41>(uint4 x, uint8_t* data, uin
   const int lane = lane_id();
   const uint32_t amax = group_max_u32<4>(absmax_bf16x8(x));     // 32 dims = 4 lanes
   const int E = ue8m0_from_amax_bits(amax << 16);
-  const uint32_t h[8] = {x.x & 0xFFFFu, x.x >> 16, x.y & 0xFFFFu, x.y >> 16,
-                         x.z & 0xFFFFu, x.z >> 16, x.w & 0xFFFFu, x.w >> 16};
-  uint32_t c[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) c[k] = fp8_from_bf16(h[k], E);
-  const uint32_t w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-  const uint32_t w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  const uint32_t w0 = fp8x4_scaled(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y), E);
+  const uint32_t w1 = fp8x4_scaled(bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w), E);
   // scale bytes: group g's E sits on lanes 4g..4g+3; lane 16k+12 packs the
   // bytes of groups 4k..4k+3 and the four packing lanes store 16 B
   const uint32_t sw = pack4_bytes_shr<4>((uint32_t)E);
@@ -86,13 +81,8 @@ __device__ __forceinline__ void store_row_wave<kV4>(uint4 x, uint8_t* data, uint
   const int lane = lane_id();
   const uint32_t amax = group_max_u32<8>(absmax_bf16x8(x));     // 64 dims = 8 lanes
   const int E = ue8m0_from_amax_bits(amax << 16);
-  const uint32_t h[8] = {x.x & 0xFFFFu, x.x >> 16, x.y & 0xFFFFu, x.y >> 16,
-                         x.z & 0xFFFFu, x.z >> 16, x.w & 0xFFFFu, x.w >> 16};
-  uint32_t c[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) c[k] = fp8_from_bf16(h[k], E);
-  const uint32_t w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-  const uint32_t w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  const uint32_t w0 = fp8x4_scaled(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y), E);
+  const uint32_t w1 = fp8x4_scaled(bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w), E);
   uint32_t sc[2];
   collect_scale_bytes<2, 8>((uint32_t)E, sc);     // lanes 0, 8, .., 56; the 8th is rope
   sc[1] &= 0x00FFFFFFu;                            // pad byte = 0
@@ -110,18 +100,21 @@ __device__ __forceinline__ void store_row_wave<kV41Fp4>(uint4 x, uint8_t* data, 
                                                         bool write) {
   const int lane = lane_id();
   const uint32_t amax = group_max_u32<2>(absmax_bf16x8(x));     // 16 dims = 2 lanes
-  // scale = e4m3(amax / 6), fp32 division correctly rounded
-  const float q = __fdiv_rn(__uint_as_float(amax << 16), 6.0f);
+  // scale = e4m3(amax / 6), the fp32 quotient correctly rounded
+  const float q = div_by_rcp(__uint_as_float(amax << 16), 6.0f, 0x1.555556p-3f);
   const uint32_t sc = e4m3_satfinite(q);
   const float s = e4m3_to_f32(sc);
   const float rs = __builtin_amdgcn_rcpf(s);
   const float xf[8] = {bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y),
                        bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
+  float qf[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) qf[k] = div_by_rcp(xf[k], s, rs);
   uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fp4_quotient(xf[0], rs), fp4_quotient(xf[1], rs), 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fp4_quotient(xf[2], rs), fp4_quotient(xf[3], rs), 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fp4_quotient(xf[4], rs), fp4_quotient(xf[5], rs), 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fp4_quotient(xf[6], rs), fp4_quotient(xf[7], rs), 1.0f, 3);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, qf[0], qf[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, qf[2], qf[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, qf[4], qf[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, qf[6], qf[7], 1.0f, 3);
   w = sc == 0 ? 0u : w;                            // zero scale: all codes 0
   // scale bytes: group g's code sits on lanes 2g, 2g+1; lane 8k+6 packs the
   // bytes of groups 4k..4k+3 and the eight packing lanes store 32 B

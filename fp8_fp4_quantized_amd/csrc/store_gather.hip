@@ -74,106 +74,144 @@ __global__ __launch_bounds__(kBlock) void store_rows_kernel(StoreParams p) {
 }
 
 // ------------------------------------------------------------------ DCP ids
-// One workgroup per row of ids, kFilterPerLane consecutive ids per lane
-// (2048 ids per pass): every lane tests its ids for ownership and looks up
-// their pages (all loads in flight together), the workgroup scans the lanes'
-// kept counts (shuffles within a wave, LDS across the four waves),
-// and each lane writes its kept slots at its offset; the row ends in -1.
-constexpr int kFilterPerLane = 8;
-constexpr int kFilterPass = kBlock * kFilterPerLane;
+// Persistent workgroups walk work units of 2048 ids (a row of k ids is
+// ceil(k / 2048) units, taken in order by one workgroup).  Wave w of a
+// workgroup takes ids [512 w, 512 w + 512) of the unit, 64 consecutive ids
+// per load so every load is one contiguous 256 B.  An id's place among the
+// kept ones is its lane count in the chunk's ballot, plus the chunks before
+// it in the wave, plus the earlier waves (through LDS), plus the row's
+// earlier units.  The ids of the next unit are loaded before the current one
+// is processed, so their latency overlaps its page-table reads and stores.
+constexpr int kFilterChunks = 8;                          // 64-id loads per lane
+constexpr int kFilterUnit = kBlock * kFilterChunks;       // 2048 ids
+
+struct FilterUnit {
+  int32_t v[kFilterChunks];   // this lane's ids (-1 past the row)
+  int32_t req;                // the row's request
+  bool valid;                 // the row is not a padding token
+};
+
+// the ids and row data of work unit u, loaded ahead of their use
+__device__ __forceinline__ FilterUnit load_unit(const DcpFilterParams& p, int64_t u,
+                                                int32_t units_per_row, int wid, int lane) {
+  FilterUnit r;
+  const int64_t t = u / units_per_row;
+  const int32_t s0 = (int32_t)(u - t * units_per_row) * kFilterUnit;
+  r.valid = p.valid == nullptr || ld_ro(p.valid + t) != 0;
+  r.req = ld_ro(p.token_to_req + t);
+  if (p.k == 0) {                                         // no ids: nothing to read
+#pragma unroll
+    for (int e = 0; e < kFilterChunks; ++e) r.v[e] = -1;
+    return r;
+  }
+  const int32_t* row = p.ids + t * p.ids_stride;
+#pragma unroll
+  for (int e = 0; e < kFilterChunks; ++e) {
+    const int32_t i = s0 + kLanes * (kFilterChunks * wid + e) + lane;
+    const int32_t v = __builtin_nontemporal_load(row + (i < p.k ? i : p.k - 1));
+    r.v[e] = i < p.k ? v : -1;
+  }
+  return r;
+}
 
 __global__ __launch_bounds__(kBlock) void dcp_filter_kernel(DcpFilterParams p) {
-  __shared__ int32_t wave_cnt[kWavesPerBlock];
+  __shared__ int32_t wave_cnt[2][kWavesPerBlock];
   const int lane = lane_id(), wid = threadIdx.x >> 6;
   const int kl = p.interleave_log2;
   const uint32_t kmask = (1u << kl) - 1, pmask = (1u << p.page_bits) - 1;
   const uint32_t world = (uint32_t)p.world, rank = (uint32_t)p.rank;
-  for (int64_t t = blockIdx.x; t < p.T; t += gridDim.x) {
-    bool keep = p.valid == nullptr || ld_ro(p.valid + t) != 0;
-    const int32_t req = ld_ro(p.token_to_req + t);
+  const int32_t units_per_row = p.k > 0 ? (p.k + kFilterUnit - 1) / kFilterUnit : 1;
+  const int64_t n_units = p.T * units_per_row;
+  int64_t u = blockIdx.x;
+  if (u >= n_units) return;
+  FilterUnit cur = load_unit(p, u, units_per_row, wid, lane);
+  int32_t cnt = 0;                                    // kept so far in the row
+  int parity = 0;                                     // LDS buffer of the next scan
+  for (; u < n_units; u += gridDim.x) {
+    const int64_t t = u / units_per_row;
+    const int32_t part = (int32_t)(u - t * units_per_row);
+    const int64_t un = u + gridDim.x;                 // next unit: its loads in flight now
+    const FilterUnit nxt = load_unit(p, un < n_units ? un : u, units_per_row, wid, lane);
+    if (part == 0) cnt = 0;
+    const int32_t req = cur.req;
+    bool keep = cur.valid;
     if (keep && (req < 0 || req >= p.n_req)) {
-      if (threadIdx.x == 0 && p.status != nullptr) atomicOr(p.status, kStReqRange);
+      if (part == 0 && threadIdx.x == 0 && p.status != nullptr) atomicOr(p.status, kStReqRange);
       keep = false;
     }
     int32_t* out = p.out_slots + t * p.out_stride;
-    int32_t cnt = 0;                                   // kept so far (workgroup-uniform)
-    if (keep) {
-      const int32_t* row = p.ids + t * p.ids_stride;
+    if (keep && p.k > 0) {
       const int32_t* bt = p.block_table + (int64_t)req * p.bt_stride;
-      for (int32_t s0 = 0; s0 < p.k; s0 += kFilterPass) {
-        const int32_t base = s0 + (int32_t)threadIdx.x * kFilterPerLane;
-        int32_t id[kFilterPerLane], lp[kFilterPerLane], u[kFilterPerLane], pg[kFilterPerLane];
+      int32_t lp[kFilterChunks], uo[kFilterChunks], pg[kFilterChunks];
 #pragma unroll
-        for (int e = 0; e < kFilterPerLane; ++e) {
-          const int32_t i = base + e;
-          const int32_t v = row[i < p.k ? i : p.k - 1];
-          id[e] = i < p.k ? v : -1;
-        }
-        // ownership and the page-table entry to read (entry 0 when unused)
-#pragma unroll
-        for (int e = 0; e < kFilterPerLane; ++e) {
-          lp[e] = -1;
-          u[e] = 0;
-          if (id[e] >= 0) {
-            const uint32_t run = (uint32_t)id[e] >> kl;
-            const uint32_t turn = run / world;
-            if (run - turn * world == rank) {
-              u[e] = (int32_t)((turn << kl) | ((uint32_t)id[e] & kmask));
-              lp[e] = u[e] >> p.page_bits;
-            }
+      for (int e = 0; e < kFilterChunks; ++e) {
+        const int32_t id = cur.v[e];
+        lp[e] = -1;
+        uo[e] = 0;
+        if (id >= 0) {
+          const uint32_t run = (uint32_t)id >> kl;
+          const uint32_t turn = run / world;
+          if (run - turn * world == rank) {
+            uo[e] = (int32_t)((turn << kl) | ((uint32_t)id & kmask));
+            lp[e] = uo[e] >> p.page_bits;
           }
         }
-#pragma unroll
-        for (int e = 0; e < kFilterPerLane; ++e) pg[e] = bt[lp[e] >= 0 && lp[e] < p.bt_stride ? lp[e] : 0];
-        int32_t slot[kFilterPerLane], n = 0, bad = 0;
-#pragma unroll
-        for (int e = 0; e < kFilterPerLane; ++e) {
-          slot[e] = -1;
-          if (lp[e] >= 0) {
-            if (lp[e] >= p.bt_stride) {
-              bad |= kStPtRange;
-            } else if (pg[e] < 0 || pg[e] >= p.num_pages) {
-              bad |= kStPageRange;
-            } else {
-              slot[e] = (pg[e] << p.page_bits) | (int32_t)((uint32_t)u[e] & pmask);
-              ++n;
-            }
-          }
-        }
-        if (bad != 0 && p.status != nullptr) atomicOr(p.status, bad);
-        // exclusive offset of this lane's kept ids within the pass
-        int32_t inc = n;
-#pragma unroll
-        for (int d = 1; d < kLanes; d <<= 1) {
-          const int32_t v = __shfl_up(inc, d);
-          if (lane >= d) inc += v;
-        }
-        if (lane == kLanes - 1) wave_cnt[wid] = inc;
-        __syncthreads();
-        int32_t before = 0, total = 0;
-#pragma unroll
-        for (int w = 0; w < kWavesPerBlock; ++w) {
-          const int32_t c = wave_cnt[w];
-          before += w < wid ? c : 0;
-          total += c;
-        }
-        int32_t o = cnt + before + inc - n;
-#pragma unroll
-        for (int e = 0; e < kFilterPerLane; ++e) {
-          if (slot[e] >= 0) out[o++] = slot[e];
-        }
-        cnt += total;
-        __syncthreads();                                 // wave_cnt is reused
       }
+#pragma unroll
+      for (int e = 0; e < kFilterChunks; ++e)
+        pg[e] = bt[lp[e] >= 0 && lp[e] < p.bt_stride ? lp[e] : 0];
+      int32_t slot[kFilterChunks], bad = 0, wave_total = 0;
+      uint64_t m[kFilterChunks];
+#pragma unroll
+      for (int e = 0; e < kFilterChunks; ++e) {
+        slot[e] = -1;
+        if (lp[e] >= 0) {
+          if (lp[e] >= p.bt_stride) {
+            bad |= kStPtRange;
+          } else if (pg[e] < 0 || pg[e] >= p.num_pages) {
+            bad |= kStPageRange;
+          } else {
+            slot[e] = (pg[e] << p.page_bits) | (int32_t)((uint32_t)uo[e] & pmask);
+          }
+        }
+        m[e] = __ballot(slot[e] >= 0);
+        wave_total += (int32_t)__builtin_popcountll(m[e]);
+      }
+      if (bad != 0 && p.status != nullptr) atomicOr(p.status, bad);
+      if (lane == 0) wave_cnt[parity][wid] = wave_total;
+      __syncthreads();
+      int32_t before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        const int32_t c = wave_cnt[parity][w];
+        before += w < wid ? c : 0;
+        total += c;
+      }
+      int32_t off = cnt + before;
+#pragma unroll
+      for (int e = 0; e < kFilterChunks; ++e) {
+        const int32_t pos = (int32_t)__builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], 0u));
+        if (slot[e] >= 0) out[off + pos] = slot[e];
+        off += (int32_t)__builtin_popcountll(m[e]);
+      }
+      cnt += total;
+      parity ^= 1;        // the next scan writes the other buffer: a wave that
+                          // reaches it has left this one's reads behind
     }
-    for (int32_t i = cnt + (int32_t)threadIdx.x; i < p.k; i += kBlock) out[i] = -1;
-    if (threadIdx.x == 0) p.out_lens[t] = cnt;
+    if (part == units_per_row - 1) {                  // the row is complete
+      for (int32_t i = cnt + (int32_t)threadIdx.x; i < p.k; i += kBlock) out[i] = -1;
+      if (threadIdx.x == 0) p.out_lens[t] = cnt;
+    }
+    cur = nxt;
   }
 }
 
 // ------------------------------------------------------------------ gather
-// rows handled together by one wave per loop trip
+// rows handled together by one wave per loop trip, and ids one wave
+// resolves per batch
 constexpr int kGatherUnroll = 8;
+constexpr int kGatherBatch = 32;
 
 template <int L> struct LaneCodes;          // this lane's share of a row
 template <> struct LaneCodes<kV41> { uint2 codes; uint32_t scale; };
@@ -183,21 +221,24 @@ template <> struct LaneCodes<kV4> { uint4 raw; uint32_t scale; };
 template <int L>
 __device__ __forceinline__ LaneCodes<L> load_lane(const PagedKV<L>& kv, int64_t slot, int lane);
 
+// Plain (cached) loads: a gathered row's scale part shares its cache line
+// with the scale parts of the page's other rows, which later ids of the
+// batch often select.  (Non-temporal loads measured slower.)
 template <>
 __device__ __forceinline__ LaneCodes<kV41> load_lane<kV41>(const PagedKV<kV41>& kv, int64_t slot,
                                                            int lane) {
   LaneCodes<kV41> r;
-  const u32x2 c = __builtin_nontemporal_load((const u32x2*)(kv.data(slot) + 8 * lane));
+  const u32x2 c = *(const u32x2*)(kv.data(slot) + 8 * lane);
   r.codes = make_uint2(c.x, c.y);
-  r.scale = __builtin_nontemporal_load(kv.scale(slot) + (lane >> 2));
+  r.scale = kv.scale(slot)[lane >> 2];
   return r;
 }
 template <>
 __device__ __forceinline__ LaneCodes<kV41Fp4> load_lane<kV41Fp4>(const PagedKV<kV41Fp4>& kv,
                                                                  int64_t slot, int lane) {
   LaneCodes<kV41Fp4> r;
-  r.codes = __builtin_nontemporal_load((const uint32_t*)(kv.data(slot) + 4 * lane));
-  r.scale = __builtin_nontemporal_load(kv.scale(slot) + (lane >> 1));
+  r.codes = *(const uint32_t*)(kv.data(slot) + 4 * lane);
+  r.scale = kv.scale(slot)[lane >> 1];
   return r;
 }
 template <>
@@ -206,11 +247,11 @@ __device__ __forceinline__ LaneCodes<kV4> load_lane<kV4>(const PagedKV<kV4>& kv,
   LaneCodes<kV4> r;
   const uint8_t* d = kv.data(slot);
   if (lane < kRopeLane0) {
-    const u32x2 c = __builtin_nontemporal_load((const u32x2*)(d + 8 * lane));
+    const u32x2 c = *(const u32x2*)(d + 8 * lane);
     r.raw = make_uint4(c.x, c.y, 0u, 0u);
-    r.scale = __builtin_nontemporal_load(kv.scale(slot) + (lane >> 3));
+    r.scale = kv.scale(slot)[lane >> 3];
   } else {
-    r.raw = ld_u4_nt(d + kNope + 16 * (lane - kRopeLane0));
+    r.raw = ld_u4(d + kNope + 16 * (lane - kRopeLane0));
     r.scale = 0;
   }
   return r;
@@ -232,11 +273,12 @@ __device__ __forceinline__ uint4 decode_lane<kV4>(const LaneCodes<kV4>& c, int l
   return dq_fp8x8(make_uint2(c.raw.x, c.raw.y), c.scale);
 }
 
-// A wave takes the rows of the gather 64 at a time: lane i reads id i of the
-// batch and resolves it to a physical slot (one vector load of ids, one of
-// page-table entries), then the rows are expanded kGatherUnroll at a time,
-// their slots broadcast with v_readlane, all their loads issued before any
-// store.
+// A wave takes the rows of the gather kGatherBatch at a time: lane i reads
+// id i of the batch and resolves it to a physical slot (one vector load of
+// ids, one of page-table entries), then the rows are expanded kGatherUnroll
+// at a time, their slots broadcast with v_readlane, all their loads issued
+// before any store.  32-id batches give 8192 waves for 262,144 ids, about
+// one resident round of the chip (measured faster than 16, 48 or 64).
 template <int L>
 __global__ __launch_bounds__(kBlock) void dequant_gather_kernel(GatherParams p) {
   const PagedKV<L> kv = paged<L>(p.cache);
@@ -245,12 +287,12 @@ __global__ __launch_bounds__(kBlock) void dequant_gather_kernel(GatherParams p) 
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const int32_t page_mask = (1 << p.cache.page_bits) - 1;
 
-  for (int64_t b0 = wave0 * kLanes; b0 < p.n; b0 += nwaves * kLanes) {
+  for (int64_t b0 = wave0 * kGatherBatch; b0 < p.n; b0 += nwaves * kGatherBatch) {
     // ---- resolve this lane's id to a slot (-1: zero row)
     const int64_t r = b0 + lane;
     int32_t slot = -1;
     int32_t bad = 0;
-    if (r < p.n) {
+    if (lane < kGatherBatch && r < p.n) {
       const int32_t id = p.ids[r];
       if (id >= 0) {
         if (p.page_table != nullptr) {
@@ -275,7 +317,7 @@ __global__ __launch_bounds__(kBlock) void dequant_gather_kernel(GatherParams p) 
     if (bad != 0 && p.status != nullptr) atomicOr(p.status, bad);
 
     // ---- expand the batch's rows
-    const int cnt = (int)(p.n - b0 < kLanes ? p.n - b0 : kLanes);
+    const int cnt = (int)(p.n - b0 < kGatherBatch ? p.n - b0 : kGatherBatch);
     for (int j = 0; j < cnt; j += kGatherUnroll) {
       int32_t s[kGatherUnroll];
       LaneCodes<L> c[kGatherUnroll];
@@ -330,11 +372,13 @@ hipError_t launch_store_rows(const StoreParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_dcp_filter(const DcpFilterParams& p, hipStream_t stream) {
-  return launch(dcp_filter_kernel, grid_for(p.T, 1, 16384), p, stream);
+  // persistent: six workgroups per compute unit (measured best of 512..4096)
+  const int64_t units = p.T * (p.k > 0 ? (p.k + kFilterUnit - 1) / kFilterUnit : 1);
+  return launch(dcp_filter_kernel, grid_for(units, 1, 1536), p, stream);
 }
 
 hipError_t launch_dequant_gather(const GatherParams& p, hipStream_t stream) {
-  int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * kLanes, 2048);
+  int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * kGatherBatch, 8192);
   if (launch_tuning().gather_blocks > 0) blocks = launch_tuning().gather_blocks;
   switch (p.cache.layout) {
     case kV41: return launch(dequant_gather_kernel<kV41>, blocks, p, stream);

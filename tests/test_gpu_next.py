@@ -345,3 +345,75 @@ def test_prefill_compress_graph_replay(K):
                     layout=layout, page_size=ps)
                 assert st_o == 0 and int(replay[4][0]) == 0
                 assert_latent_close(replay[1].view(np.uint16)[:n], lat_o)
+
+
+# ================================================================= quantizer, exhaustive
+def _groups_to_rows(groups, gsize):
+    """pack groups of gsize bf16 values into 512-dim rows (zero padded)."""
+    per_row = 512 // gsize
+    n = -(-len(groups) // per_row)
+    rows = np.zeros((n * per_row, gsize), np.uint16)
+    rows[:len(groups)] = groups
+    return rows.reshape(n, 512)
+
+
+def _all_finite_bf16_upto(a):
+    """every finite bf16 pattern (both signs) with magnitude <= a."""
+    b = spec.all_bf16()
+    v = np.abs(spec.bf16_value(b))
+    return b[v <= a]
+
+
+def _store_and_compare(K, layout, rows):
+    ps = 64
+    n = rows.shape[0]
+    npages = n // ps + 2
+    rb = oracle.layout_bytes(layout)[2]
+    loc = (np.arange(n) + ps).astype(np.int32)
+    hc = np.zeros((npages, ps * rb), np.uint8)
+    dc = dev(hc)
+    assert oracle.store_rows(hc, layout, ps, rows, loc) == 0
+    K.kvc_store_rows(K.Cache(dc, layout, ps), dev(rows), dev(loc))
+    torch.cuda.synchronize()
+    g = host(dc)
+    bad = np.argwhere(g != hc)
+    assert bad.size == 0, bad[:5]
+
+
+def test_fp8_quantizer_every_value_every_exponent(K):
+    """Every finite bf16 value under every ue8m0 exponent it can meet: group g
+    holds the amax that gives exponent E and then every bf16 of magnitude up
+    to it; the cache bytes equal the oracle's."""
+    _say("fp8 quantizer exhaustive")
+    top = float(spec.bf16_value(np.uint16(0x7F7F)))
+    groups = []
+    for E in range(114, 248):
+        a = min(448.0 * 2.0 ** (E - 127), top)
+        A = spec.bf16_nearest(np.array([a]))[0]
+        if spec.bf16_value(A) > a:                     # largest bf16 not above a
+            A = np.uint16(A - 1)
+        assert oracle.ue8m0(np.array([spec.bf16_value(A)], np.float32))[0] == E
+        xs = _all_finite_bf16_upto(float(spec.bf16_value(A)))
+        pad = (-len(xs)) % 31
+        xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, 31)
+        groups.append(np.concatenate([np.full((len(xs), 1), A, np.uint16), xs], axis=1))
+    rows = _groups_to_rows(np.concatenate(groups), 32)
+    _store_and_compare(K, "V41", rows)
+
+
+def test_fp4_quantizer_every_value_every_scale(K):
+    """Every finite bf16 value under every positive finite e4m3 scale it can
+    meet (|x| <= 6 s, the group amax 6 s setting the scale s)."""
+    _say("fp4 quantizer exhaustive")
+    groups = []
+    for c in range(1, 0x7F):
+        s = float(oracle.e4m3_decode(np.array([c], np.uint8))[0])
+        A = spec.bf16_nearest(np.array([6.0 * s]))[0]
+        assert spec.bf16_value(A) == 6.0 * s
+        assert oracle.fp4_scale(np.array([6.0 * s], np.float32))[0] == c
+        xs = _all_finite_bf16_upto(6.0 * s)
+        pad = (-len(xs)) % 15
+        xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, 15)
+        groups.append(np.concatenate([np.full((len(xs), 1), A, np.uint16), xs], axis=1))
+    rows = _groups_to_rows(np.concatenate(groups), 16)
+    _store_and_compare(K, "V41_FP4", rows)

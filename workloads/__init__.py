@@ -30,7 +30,7 @@ __all__ = [
     "norm_weight", "rope_freqs", "outlier_rows", "random_pages",
     "paged_cache_shape", "random_cache_bytes", "compress_case", "decode_case",
     "store_case", "gather_case", "ragged_lengths", "verify_case", "rope_store_case",
-    "dcp_ids_case", "per_rank_page_tables",
+    "dcp_ids_case", "per_rank_page_tables", "workload_c4_id_sets",
     "workload_c1", "workload_c2", "workload_c3", "workload_c4", "workload_c5",
 ]
 
@@ -420,6 +420,19 @@ def workload_c4(n_ids: int = 262144, logical_pages: int = 16384, page_size: int 
     page table, 262,144 distinct gather ids."""
     return gather_case(BASE_SEED + 4, logical_pages, page_size, n_ids,
                        row_bytes=528, data_bytes=512, scale_bytes=16)
+
+
+def workload_c4_id_sets(count: int, n_ids: int = 262144, logical_pages: int = 16384,
+                        page_size: int = 64):
+    """``count`` id lists of the C4 gather: the workload's own list first,
+    then lists of the same size drawn the same way from other seeds (so that
+    consecutive gathers of a timing loop read different rows)."""
+    sets = [workload_c4(n_ids, logical_pages, page_size)["ids"]]
+    for j in range(1, count):
+        rng = np.random.default_rng(BASE_SEED + 4 + 1000 * j)
+        sets.append(rng.choice(logical_pages * page_size, size=n_ids,
+                               replace=False).astype(np.int32))
+    return sets
 
 
 def workload_c5(batch: int = 1024):
