@@ -91,7 +91,8 @@ def measure_next_rows(kvc, W, d, dev, stream):
 
     def entry(name, secs, nbytes, units, unit):
         res[name] = {"us": secs * 1e6, "bytes": int(nbytes), "gbps": nbytes / secs / 1e9,
-                     "frac": nbytes / secs / 1e9 / HBM_PEAK_GBS, unit: units / secs}
+                     "frac": nbytes / secs / 1e9 / HBM_PEAK_GBS, unit: units / secs,
+                     "traffic": measured_traffic(name)}
 
     # verify: 1024 slots x 4 drafts, ring of 3, V41_FP4 cache through page tables
     vc = W.verify_case(20261206, 1024, draft_len=4, ratio=2, page_size=64, max_pos=4096,

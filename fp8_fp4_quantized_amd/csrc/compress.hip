@@ -58,16 +58,17 @@ __device__ __forceinline__ int64_t ring_row(const CompressParams& p, int32_t b, 
 }
 
 // registers of one row's inputs: this lane's 16 B of the pair's kv and score
-// rows and (rope lanes) its 8 rotary-table entries
+// rows and one entry of the row's rotary-table line (lane k holds entry k;
+// the rope lanes gather theirs with lane shuffles when they rotate)
 struct RowIn {
   uint4 k0, s0, k1, s1;
-  float4 f0, f1;
+  float f;
 };
 
 // Every lane issues the same loads whatever the row (the first token comes
-// from the pending state or the buffer by an address select, and the lanes
-// that hold no rope dims read a rope lane's table entries), so the count of
-// memory operations in flight is fixed and the compiler's waits stay exact.
+// from the pending state or the buffer by an address select), so the count
+// of memory operations in flight is fixed and the compiler's waits stay
+// exact.
 template <int RATIO>
 __device__ __forceinline__ RowIn load_row(const CompressParams& p, const RowJob& j) {
   const int lane = lane_id();
@@ -84,9 +85,7 @@ __device__ __forceinline__ RowIn load_row(const CompressParams& p, const RowJob&
     in.s0 = ld_u4(s0 + dim0);
   }
   const int64_t rp = j.rot_pos < 0 ? 0 : (j.rot_pos >= p.max_pos ? p.max_pos - 1 : j.rot_pos);
-  const float* fr = p.freqs + rp * kRope + kDimsPerLane * ((lane - kRopeLane0) & 7);
-  in.f0 = *(const float4*)fr;
-  in.f1 = *(const float4*)(fr + 4);
+  in.f = p.freqs[rp * kRope + lane];
   return in;
 }
 
@@ -145,15 +144,19 @@ __device__ __forceinline__ void finish_row(const CompressParams& p, const PagedK
                                pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7]));
   const bool lat_ok = j.latent_idx < p.max_out_rows;
   if (lat_ok) {
-    st_u4(p.latent + j.latent_idx * p.latent_stride + dim0, lat);
+    st_u4_nt(p.latent + j.latent_idx * p.latent_stride + dim0, lat);
   } else {
     raise_status(p.status, kStLatentRange);
   }
 
-  // ---- RoPE on the last 64 dims: pairs (2i, 2i+1) times (cos, sin)
+  // ---- RoPE on the last 64 dims: pairs (2i, 2i+1) times (cos, sin); rope
+  // lane 56 + m takes table entries 8m .. 8m + 7 from the lanes holding them
+  float cs[8];
+  const int src = kDimsPerLane * ((lane - kRopeLane0) & 7);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cs[i] = __int_as_float(__shfl(__float_as_int(in.f), src + i));
   uint4 z = lat;
   if (lane >= kRopeLane0) {
-    const float cs[8] = {in.f0.x, in.f0.y, in.f0.z, in.f0.w, in.f1.x, in.f1.y, in.f1.z, in.f1.w};
     float o[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -417,3 +417,36 @@ def test_fp4_quantizer_every_value_every_scale(K):
         groups.append(np.concatenate([np.full((len(xs), 1), A, np.uint16), xs], axis=1))
     rows = _groups_to_rows(np.concatenate(groups), 16)
     _store_and_compare(K, "V41_FP4", rows)
+
+
+# ================================================================= launch shapes
+@pytest.mark.parametrize("tile_rows", [1, 2, 4])
+@pytest.mark.parametrize("layout,ratio,slots", [("V41_FP4", 2, 9), ("V41", 1, 9), ("V4", 2, 90)])
+def test_prefill_every_tile_shape(K, tile_rows, layout, ratio, slots):
+    """The prefill compressor under each work-item shape (rows per item 1, 2
+    or 4), small (<= 64 slots) and large slot counts: same rows as the
+    oracle."""
+    _say("tile shape", tile_rows, layout, ratio, slots)
+    rng = np.random.default_rng(300 + slots + ratio)
+    lengths = rng.integers(0, 90, size=slots)
+    lengths[rng.random(slots) < 0.15] = 0
+    P = rng.integers(0, 120, size=slots)
+    case = W.compress_case(310 + tile_rows, lengths, start_pos=P, ratio=ratio, page_size=8,
+                           fused=True, gap=2)
+    K.kvc_set_launch_shape(0, 0, tile_rows)
+    try:
+        r = run_compress(K, case, layout, ratio, oracle.PREFILL)
+    finally:
+        K.kvc_set_launch_shape(0, 0, 0)
+    lat, slots_ = [], []
+    L = 0
+    for b in range(len(lengths)):
+        n, p0 = int(lengths[b]), int(P[b])
+        qs = range(p0, p0 + n) if ratio == 1 else [q for q in range(p0, p0 + n) if q % 2 == 1]
+        for q in qs:
+            c = q if ratio == 1 else q // 2
+            slots_.append(int(case["page_table"][b, c // 8]) * 8 + c % 8)
+            lat.append(L)
+            L += 1
+    assert r["n_rows"] == L
+    check_compress(r, layout, 8, slots_, lat)
