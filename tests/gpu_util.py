@@ -111,13 +111,14 @@ def assert_rows_close(layout: str, gd, gs, od, os_, ref_vals):
 
 # --------------------------------------------------------------- compressor runs
 def run_compress(K, case, layout, ratio, mode, fused=True, eps=None, max_out_rows=None,
-                 out_loc=None, page_table="case", want_state=True, cache_fill=0xA5, **extra):
+                 out_loc=None, page_table="case", want_state=True, cache_fill=0xA5,
+                 page_stride=None, **extra):
     """run oracle and GPU on the same inputs; returns dict of both sides.
     ``extra``: draft_len, ring_slots and dcp_* arguments, passed to both."""
     ps = case["page_size"]
     db, sb, rb, _ = oracle.layout_bytes(layout)
     eps = case["eps"] if eps is None else eps
-    hc = np.full((case["num_pages"], ps * rb), cache_fill, np.uint8)
+    hc = np.full((case["num_pages"], page_stride or ps * rb), cache_fill, np.uint8)
     dc = dev(hc)
     state_h = case["state"].copy()
     state_d = dev(case["state"])

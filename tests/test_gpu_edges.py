@@ -1,0 +1,188 @@
+"""Edge cases of the HIP path against the oracle, through the C ABI: the
+largest prefill batch, the smallest and largest pages, strided buffers,
+ragged gather counts, the longest draft and decode context parallelism at a
+wide group.  Same bar as the other parity tests (bytes bit-exact; fused
+outputs within the stated tolerance)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_util import check_compress, dev, host, run_compress
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import fp8_fp4_quantized_amd as k
+    return k
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _prefill_rows(case, ratio, lengths, P, ps):
+    lat, slots, L = [], [], 0
+    for b in range(len(lengths)):
+        n, p0 = int(lengths[b]), int(P[b])
+        if n <= 0 or p0 < 0:
+            continue
+        qs = range(p0, p0 + n) if ratio == 1 else [q for q in range(p0, p0 + n) if q % 2 == 1]
+        for q in qs:
+            c = q if ratio == 1 else q // 2
+            slots.append(int(case["page_table"][b, c // ps]) * ps + c % ps)
+            lat.append(L)
+            L += 1
+    return lat, slots
+
+
+@pytest.mark.parametrize("ratio", [1, 2])
+def test_prefill_largest_slot_count(K, ratio):
+    """8191 request slots (the largest prefill batch: two LDS tables of 8192
+    ints), lengths 0..3, odd and even starts."""
+    _say("prefill 8191 slots", ratio)
+    rng = np.random.default_rng(400 + ratio)
+    S = 8191
+    lengths = rng.integers(0, 4, size=S)
+    P = rng.integers(0, 9, size=S)
+    case = W.compress_case(401 + ratio, lengths, start_pos=P, ratio=ratio, page_size=4,
+                           fused=True, pt_slack=0, spare_pages=1)
+    r = run_compress(K, case, "V41_FP4", ratio, oracle.PREFILL)
+    lat, slots = _prefill_rows(case, ratio, lengths, P, 4)
+    assert r["n_rows"] == len(lat)
+    check_compress(r, "V41_FP4", 4, slots, lat)
+
+
+@pytest.mark.parametrize("ps", [1, 4096])
+@pytest.mark.parametrize("layout", ["V4", "V41", "V41_FP4"])
+def test_page_size_extremes(K, ps, layout):
+    """page_size 1 (every row its own page; V4's 584-byte page padded to a
+    592-byte stride) and 4096: store, compress and gather."""
+    _say("page size", ps, layout)
+    rng = np.random.default_rng(410 + ps)
+    lengths = [300, 0, 77, 1]
+    P = [0, 0, 3, 10]
+    db, sb, rb, _ = oracle.layout_bytes(layout)
+    stride = -(-ps * rb // 16) * 16
+    case = W.compress_case(411, lengths, start_pos=P, ratio=2, page_size=ps, fused=True)
+    r = run_compress(K, case, layout, 2, oracle.PREFILL, page_stride=stride)
+    lat, slots = _prefill_rows(case, 2, lengths, P, ps)
+    check_compress(r, layout, ps, slots, lat)
+    # plain store + gather back through the physical slots just written
+    rows = W.outlier_rows(rng, len(slots))
+    loc = np.asarray(slots, np.int32)
+    hc = np.zeros((case["num_pages"], stride), np.uint8)
+    dc = dev(hc)
+    assert oracle.store_rows(hc, layout, ps, rows, loc) == 0
+    K.kvc_store_rows(K.Cache(dc, layout, ps), dev(rows), dev(loc))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dc), hc)
+    ids = np.concatenate([loc[::-1], [-1, 0]]).astype(np.int32)
+    want, st = oracle.dequant_gather(hc, layout, ps, None, ids)
+    out = torch.empty((ids.size, 512), dtype=torch.int16, device="cuda")
+    K.kvc_dequant_gather(K.Cache(dc, layout, ps), None, dev(ids), out)
+    torch.cuda.synchronize()
+    assert st == 0 and np.array_equal(host(out, np.uint16), want)
+
+
+def test_strided_buffers(K):
+    """separate kv and score buffers with row strides 640 and 768, latent
+    and pre-quant outputs with strides 520 and 1024, gather output stride
+    1032: the padding columns stay untouched."""
+    _say("strided buffers")
+    lengths, P = [45, 8, 0, 19], [0, 1, 0, 6]
+    case = W.compress_case(420, lengths, start_pos=P, ratio=2, page_size=16, fused=False)
+    T = case["T"]
+    kv = np.full((T, 640), 0x7F7F, np.uint16)
+    kv[:, :512] = case["kv"]
+    sc = np.full((T, 768), 0x7F7F, np.uint16)
+    sc[:, :512] = case["score"]
+    hc = np.zeros((case["num_pages"], 16 * 528), np.uint8)
+    state = case["state"].copy()
+    lat_o, pre_o, st, n = oracle.compress(
+        ratio=2, mode=oracle.PREFILL, kv=case["kv"], score=case["score"],
+        offsets=case["offsets"], start_pos=case["start_pos"], page_table=case["page_table"],
+        state=state, norm_w=case["norm_w"], eps=case["eps"], freqs=case["freqs"], cache=hc,
+        layout="V41", page_size=16)
+    dc = dev(np.zeros_like(hc))
+    lat = torch.full((n, 520), 3, dtype=torch.int16, device="cuda")
+    pre = torch.full((n, 1024), 3, dtype=torch.int16, device="cuda")
+    sd = dev(case["state"])
+    K.kvc_compress_store(ratio=2, mode=K.MODE_PREFILL, kv=dev(kv)[:, :512], score=dev(sc)[:, :512],
+                         start_pos=dev(case["start_pos"]), offsets=dev(case["offsets"]),
+                         page_table=dev(case["page_table"]), state=sd,
+                         norm_w=dev(case["norm_w"]), eps=case["eps"], freqs=dev(case["freqs"]),
+                         latent_out=lat[:, :512], prequant_out=pre[:, :512],
+                         cache=K.Cache(dc, "V41", 16))
+    torch.cuda.synchronize()
+    lg, pg = host(lat, np.uint16), host(pre, np.uint16)
+    assert np.all(lg[:, 512:] == 3) and np.all(pg[:, 512:] == 3)
+    r = dict(lat_o=lat_o, pre_o=pre_o, st_o=st, st_g=st, lat_g=lg[:, :512], pre_g=pg[:, :512],
+             cache_o=hc, cache_g=host(dc), state_o=state, state_g=host(sd, np.uint16))
+    lat_i, slots = _prefill_rows(case, 2, lengths, P, 16)
+    check_compress(r, "V41", 16, slots, lat_i)
+    ids = np.asarray(slots[:37], np.int32)
+    want, _ = oracle.dequant_gather(hc, "V41", 16, None, ids)
+    out = torch.full((ids.size, 1032), 5, dtype=torch.int16, device="cuda")
+    K.kvc_dequant_gather(K.Cache(dev(hc), "V41", 16), None, dev(ids), out[:, :512])
+    torch.cuda.synchronize()
+    g = host(out, np.uint16)
+    assert np.array_equal(g[:, :512], want) and np.all(g[:, 512:] == 5)
+
+
+@pytest.mark.parametrize("n", [1, 31, 33, 97])
+@pytest.mark.parametrize("layout", ["V4", "V41_FP4"])
+def test_gather_ragged_counts(K, n, layout):
+    """id counts that are not a multiple of the 32-id batch or the 8-row
+    unroll, through a page table."""
+    _say("gather ragged", n, layout)
+    db, sb, rb, _ = oracle.layout_bytes(layout)
+    c = W.gather_case(430 + n, 8, 16, n, rb, db, sb,
+                      scale_lo=None if layout == "V41_FP4" else 110, scale_hi=140)
+    want, st = oracle.dequant_gather(c["cache"], layout, 16, c["page_table"], c["ids"])
+    out = torch.full((n + 1, 512), 9, dtype=torch.int16, device="cuda")
+    K.kvc_dequant_gather(K.Cache(dev(c["cache"]), layout, 16), dev(c["page_table"]),
+                         dev(c["ids"]), out[:n])
+    torch.cuda.synchronize()
+    g = host(out, np.uint16)
+    assert st == 0 and np.array_equal(g[:n], want) and np.all(g[n] == 9)
+
+
+def test_verify_longest_draft(K):
+    """draft_len 64 (the largest), ring of 33 entries (rollback-safe)."""
+    _say("verify draft 64")
+    case = W.verify_case(440, 6, draft_len=64, ratio=2, page_size=16, max_pos=400,
+                         ring_slots=33)
+    r = run_compress(K, case, "V41", 2, oracle.VERIFY, page_table=case["page_table"],
+                     draft_len=64, ring_slots=33)
+    lat, slots = [], []
+    for b in range(6):
+        for j in range(64):
+            q = int(case["pos"][b]) + j
+            if q % 2 == 1:
+                c = q // 2
+                slots.append(int(case["page_table"][b, c // 16]) * 16 + c % 16)
+                lat.append(b * 64 + j)
+    check_compress(r, "V41", 16, slots, lat)
+
+
+def test_dcp_decode_wide_group(K):
+    """decode through the page table with 8 ranks in runs of 8: each rank
+    stores only the rows it owns."""
+    case = W.verify_case(450, 256, draft_len=1, ratio=2, page_size=64, max_pos=4096,
+                         ring_slots=1)
+    for rank in (0, 5, 7):
+        _say("dcp decode rank", rank)
+        r = run_compress(K, case, "V41_FP4", 2, oracle.DECODE, page_table=case["page_table"],
+                         dcp_world=8, dcp_rank=rank, dcp_interleave=8)
+        lat, slots = [], []
+        for b in range(256):
+            q = int(case["pos"][b])
+            if q % 2 == 1:
+                ow, u = oracle.dcp_owner(q // 2, 8, 8)
+                slots.append(int(case["page_table"][b, u // 64]) * 64 + u % 64 if ow == rank else 0)
+                lat.append(b)
+        check_compress(r, "V41_FP4", 64, slots, lat)
