@@ -14,11 +14,13 @@ namespace kvc {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even
-// (v_cvt_pk_bf16_f32 on gfx950)
+// two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950 (converting the halves one by one costs two
+// conversions, a shift and an or)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_pk __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2_pk));
 }
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
@@ -52,7 +54,8 @@ __device__ __forceinline__ int ue8m0_from_amax_bits(uint32_t b) {
 // bf16 x and every E in 114..254 with |x| * 2^(127 - E) <= 448 (the range the
 // ue8m0 exponent of x's group guarantees) its code equals the
 // nearest-even encoding, negative zero and subnormals included (checked
-// exhaustively on the device against the definition).
+// exhaustively on the device against the definition).  With a unit scale it
+// also gives the FP4 group scale's e4m3 code of any fp32 in [0, 448].
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t fp8x4_scaled(float a, float b, float c, float d, int E) {
   const float sc = __uint_as_float((uint32_t)E << 23);
@@ -74,19 +77,6 @@ __device__ __forceinline__ float div_by_rcp(float x, float s, float rs) {
   const float q0 = x * rs;
   const float r = __builtin_fmaf(-q0, s, x);
   return __builtin_copysignf(__builtin_fmaf(r, rs, q0), x);
-}
-
-// e4m3fn code of a non-negative finite fp32, nearest even, clamped at 448
-// (0x7E).  Used for the FP4 group scale.
-__device__ __forceinline__ uint32_t e4m3_satfinite(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const int fe = (int)(u >> 23) - 120;
-  const uint32_t m = u & 0x7FFFFFu;
-  const uint32_t rn = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;
-  uint32_t normal = ((uint32_t)fe << 3) + rn;
-  normal = fe >= 16 ? 0x7Eu : (normal > 0x7Eu ? 0x7Eu : normal);
-  const uint32_t sub = (uint32_t)__builtin_rintf(f * 512.0f);   // below 2^-6: k * 2^-9
-  return fe >= 1 ? normal : sub;
 }
 
 // exact fp32 value of an e4m3fn code (NaN codes excluded by the caller)

@@ -89,15 +89,20 @@ __device__ __forceinline__ RowIn load_row(const CompressParams& p, const RowJob&
   return in;
 }
 
+// The arithmetic of one row, with no memory access and no branch, so that a
+// tile's rows can be scheduled together: pooling, RMSNorm, the pre-RoPE
+// latent, RoPE and the quantized codes.
+template <int L>
+struct RowOut {
+  uint4 lat;              // pre-RoPE latent, bf16
+  uint4 z;                // post-RoPE row fed to the quantizer, bf16
+  RowQ<L> q;              // its codes and scale bytes
+};
+
 template <int L, int RATIO>
-__device__ __forceinline__ void finish_row(const CompressParams& p, const PagedKV<L>& kv,
-                                           const float (&w)[8], const RowJob& j, const RowIn& in) {
+__device__ __forceinline__ RowOut<L> compute_row(const CompressParams& p, const float (&w)[8],
+                                                 const RowIn& in) {
   const int lane = lane_id();
-  if (j.rot_pos < 0 || j.rot_pos >= p.max_pos) {
-    raise_status(p.status, kStPosRange);
-    return;
-  }
-  const int dim0 = kDimsPerLane * lane;
 
   // ---- pooling (ratio 2): softmax over the two scores, per dim
   const uint32_t k1w[4] = {in.k1.x, in.k1.y, in.k1.z, in.k1.w};
@@ -139,37 +144,53 @@ __device__ __forceinline__ void finish_row(const CompressParams& p, const PagedK
 #pragma unroll
   for (int k = 0; k < 8; ++k) y[k] = v[k] * r * w[k];
 
-  // ---- pre-RoPE latent
-  const uint4 lat = make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]),
-                               pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7]));
-  const bool lat_ok = j.latent_idx < p.max_out_rows;
-  if (lat_ok) {
-    st_u4_nt(p.latent + j.latent_idx * p.latent_stride + dim0, lat);
-  } else {
-    raise_status(p.status, kStLatentRange);
-  }
+  RowOut<L> o;
+  o.lat = make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
+                     pack_bf16(y[6], y[7]));
 
   // ---- RoPE on the last 64 dims: pairs (2i, 2i+1) times (cos, sin); rope
   // lane 56 + m takes table entries 8m .. 8m + 7 from the lanes holding them
+  // (every lane computes, the nope lanes keep the latent)
   float cs[8];
   const int src = kDimsPerLane * ((lane - kRopeLane0) & 7);
 #pragma unroll
   for (int i = 0; i < 8; ++i) cs[i] = __int_as_float(__shfl(__float_as_int(in.f), src + i));
-  uint4 z = lat;
-  if (lane >= kRopeLane0) {
-    float o[8];
+  float rot[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = y[2 * i], b = y[2 * i + 1], c = cs[2 * i], s = cs[2 * i + 1];
-      o[2 * i] = a * c - b * s;
-      o[2 * i + 1] = a * s + b * c;
-    }
-    z = make_uint4(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
-                   pack_bf16(o[6], o[7]));
+  for (int i = 0; i < 4; ++i) {
+    const float a = y[2 * i], b = y[2 * i + 1], c = cs[2 * i], s = cs[2 * i + 1];
+    rot[2 * i] = a * c - b * s;
+    rot[2 * i + 1] = a * s + b * c;
   }
-  if (p.prequant != nullptr && lat_ok) st_u4(p.prequant + j.latent_idx * p.prequant_stride + dim0, z);
+  // per-word selects (a select of the whole vector compiles to an indexed
+  // private array)
+  const bool rope = lane >= kRopeLane0;
+  o.z.x = rope ? pack_bf16(rot[0], rot[1]) : o.lat.x;
+  o.z.y = rope ? pack_bf16(rot[2], rot[3]) : o.lat.y;
+  o.z.z = rope ? pack_bf16(rot[4], rot[5]) : o.lat.z;
+  o.z.w = rope ? pack_bf16(rot[6], rot[7]) : o.lat.w;
+  o.q = quantize_row<L>(o.z);
+  return o;
+}
 
-  // ---- quantized store at the destination slot (0: padded row, no write)
+// The stores of one computed row: latent, pre-quant copy and the quantized
+// row at its destination slot (0: padded row, no cache write), with the
+// status bits of whatever is out of range.
+template <int L>
+__device__ __forceinline__ void store_row_out(const CompressParams& p, const PagedKV<L>& kv,
+                                              const RowJob& j, const RowOut<L>& o) {
+  if (j.rot_pos < 0 || j.rot_pos >= p.max_pos) {
+    raise_status(p.status, kStPosRange);
+    return;
+  }
+  const int dim0 = kDimsPerLane * lane_id();
+  const bool lat_ok = j.latent_idx < p.max_out_rows;
+  if (lat_ok) {
+    st_u4_nt(p.latent + j.latent_idx * p.latent_stride + dim0, o.lat);
+    if (p.prequant != nullptr) st_u4(p.prequant + j.latent_idx * p.prequant_stride + dim0, o.z);
+  } else {
+    raise_status(p.status, kStLatentRange);
+  }
   bool write = j.loc_err == 0 && j.loc != 0;
   if (j.loc_err != 0) raise_status(p.status, j.loc_err);
   if (write && !kv.valid(j.loc)) {
@@ -177,7 +198,13 @@ __device__ __forceinline__ void finish_row(const CompressParams& p, const PagedK
     write = false;
   }
   const int64_t slot = write ? j.loc : 0;
-  store_row_wave<L>(z, kv.data(slot), kv.scale(slot), write);
+  store_quantized<L>(o.q, o.z, kv.data(slot), kv.scale(slot), write);
+}
+
+template <int L, int RATIO>
+__device__ __forceinline__ void finish_row(const CompressParams& p, const PagedKV<L>& kv,
+                                           const float (&w)[8], const RowJob& j, const RowIn& in) {
+  store_row_out<L>(p, kv, j, compute_row<L, RATIO>(p, w, in));
 }
 
 // the destination slot of row c of slot b through the page table
@@ -362,9 +389,14 @@ __device__ __forceinline__ void run_tile(const CompressParams& p, const PagedKV<
         j[r].loc = loc_err ? 0 : page_base + ((c_lo + r) & page_mask);
       }
     }
+    // the tile's arithmetic as one block (the rows' instruction streams
+    // interleave), then its stores
+    RowOut<L> o[kTileRows];
+#pragma unroll
+    for (int r = 0; r < kTileRows; ++r) o[r] = compute_row<L, RATIO>(p, w, in[r]);
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
-      if (c_lo + r < c_hi) finish_row<L, RATIO>(p, kv, w, j[r], in[r]);
+      if (c_lo + r < c_hi) store_row_out<L>(p, kv, j[r], o[r]);
     }
   }
   if constexpr (RATIO == 2) {
@@ -466,7 +498,7 @@ __global__ __launch_bounds__(kBlock) void compress_tokens_kernel(CompressParams 
   const float w[8] = {bf16_lo(wr.x), bf16_hi(wr.x), bf16_lo(wr.y), bf16_hi(wr.y),
                       bf16_lo(wr.z), bf16_hi(wr.z), bf16_lo(wr.w), bf16_hi(wr.w)};
   // the slot's rows two at a time, the loads of both issued before either
-  // is finished (a lone last row loads its inputs twice)
+  // is computed
   auto job = [&](int32_t jj) {
     const int64_t q = P + jj;
     RowJob r;
@@ -491,10 +523,14 @@ __global__ __launch_bounds__(kBlock) void compress_tokens_kernel(CompressParams 
     const bool two = jj + step < D;
     const RowJob j0 = job(jj);
     const RowJob j1 = two ? job(jj + step) : j0;
-    const RowIn in0 = load_row<RATIO>(p, j0);
-    const RowIn in1 = load_row<RATIO>(p, j1);
-    finish_row<L, RATIO>(p, kv, w, j0, in0);
-    if (two) finish_row<L, RATIO>(p, kv, w, j1, in1);
+    if (two) {
+      const RowIn in0 = load_row<RATIO>(p, j0);
+      const RowIn in1 = load_row<RATIO>(p, j1);
+      finish_row<L, RATIO>(p, kv, w, j0, in0);
+      finish_row<L, RATIO>(p, kv, w, j1, in1);
+    } else {
+      finish_row<L, RATIO>(p, kv, w, j0, load_row<RATIO>(p, j0));
+    }
   }
   if constexpr (RATIO == 2) {
     // an even position's token becomes the pending token of its pair, unless

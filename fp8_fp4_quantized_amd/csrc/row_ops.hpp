@@ -52,58 +52,58 @@ __device__ __forceinline__ void collect_scale_bytes(uint32_t v, uint32_t (&out)[
 }
 
 // ------------------------------------------------------------------ store_row
-// Quantize the row held by the wave (x = this lane's 8 dims) and write it to
-// `data` / `scale` (the row's parts in its page).  Every lane of the wave
-// must call this (the group reductions read neighbouring lanes); `write` is
-// wave-uniform.
+// Quantize the row held by the wave (x = this lane's 8 dims): quantize_row
+// computes this lane's code words and the packed scale bytes, with no memory
+// access and no branch, so several rows' quantization can be scheduled
+// together; store_quantized writes them to `data` / `scale` (the row's parts
+// in its page).  Every lane of the wave must call both (the group
+// reductions read neighbouring lanes); `write` is wave-uniform.
+template <int L> struct RowQ;
+template <> struct RowQ<kV41> { uint32_t w0, w1, sw; };
+template <> struct RowQ<kV41Fp4> { uint32_t w, sw; };
+template <> struct RowQ<kV4> { uint32_t w0, w1, sc0, sc1; };
+
 template <int L>
-__device__ __forceinline__ void store_row_wave(uint4 x, uint8_t* data, uint8_t* scale, bool write);
+__device__ __forceinline__ RowQ<L> quantize_row(uint4 x);
 
 template <>
-__device__ __forceinline__ void store_row_wave<kV41>(uint4 x, uint8_t* data, uint8_t* scale,
-                                                     bool write) {
-  const int lane = lane_id();
+__device__ __forceinline__ RowQ<kV41> quantize_row<kV41>(uint4 x) {
   const uint32_t amax = group_max_u32<4>(absmax_bf16x8(x));     // 32 dims = 4 lanes
   const int E = ue8m0_from_amax_bits(amax << 16);
-  const uint32_t w0 = fp8x4_scaled(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y), E);
-  const uint32_t w1 = fp8x4_scaled(bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w), E);
+  RowQ<kV41> q;
+  q.w0 = fp8x4_scaled(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y), E);
+  q.w1 = fp8x4_scaled(bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w), E);
   // scale bytes: group g's E sits on lanes 4g..4g+3; lane 16k+12 packs the
-  // bytes of groups 4k..4k+3 and the four packing lanes store 16 B
-  const uint32_t sw = pack4_bytes_shr<4>((uint32_t)E);
-  if (!write) return;
-  *(u32x2*)(data + 8 * lane) = u32x2{w0, w1};
-  if ((lane & 15) == 12) *(uint32_t*)(scale + 4 * (lane >> 4)) = sw;
+  // bytes of groups 4k..4k+3
+  q.sw = pack4_bytes_shr<4>((uint32_t)E);
+  return q;
 }
 
 template <>
-__device__ __forceinline__ void store_row_wave<kV4>(uint4 x, uint8_t* data, uint8_t* scale,
-                                                    bool write) {
-  const int lane = lane_id();
+__device__ __forceinline__ RowQ<kV4> quantize_row<kV4>(uint4 x) {
   const uint32_t amax = group_max_u32<8>(absmax_bf16x8(x));     // 64 dims = 8 lanes
   const int E = ue8m0_from_amax_bits(amax << 16);
-  const uint32_t w0 = fp8x4_scaled(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y), E);
-  const uint32_t w1 = fp8x4_scaled(bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w), E);
+  RowQ<kV4> q;
+  q.w0 = fp8x4_scaled(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y), E);
+  q.w1 = fp8x4_scaled(bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w), E);
   uint32_t sc[2];
   collect_scale_bytes<2, 8>((uint32_t)E, sc);     // lanes 0, 8, .., 56; the 8th is rope
-  sc[1] &= 0x00FFFFFFu;                            // pad byte = 0
-  if (!write) return;
-  if (lane < kRopeLane0) {
-    *(u32x2*)(data + 8 * lane) = u32x2{w0, w1};
-  } else {                                         // rope dims kept as bf16
-    st_u4(data + kNope + 16 * (lane - kRopeLane0), x);
-  }
-  if (lane == 0) *(u32x2*)scale = u32x2{sc[0], sc[1]};
+  q.sc0 = sc[0];
+  q.sc1 = sc[1] & 0x00FFFFFFu;                    // pad byte = 0
+  return q;
 }
 
 template <>
-__device__ __forceinline__ void store_row_wave<kV41Fp4>(uint4 x, uint8_t* data, uint8_t* scale,
-                                                        bool write) {
-  const int lane = lane_id();
+__device__ __forceinline__ RowQ<kV41Fp4> quantize_row<kV41Fp4>(uint4 x) {
   const uint32_t amax = group_max_u32<2>(absmax_bf16x8(x));     // 16 dims = 2 lanes
-  // scale = e4m3(amax / 6), the fp32 quotient correctly rounded
-  const float q = div_by_rcp(__uint_as_float(amax << 16), 6.0f, 0x1.555556p-3f);
-  const uint32_t sc = e4m3_satfinite(q);
-  const float s = e4m3_to_f32(sc);
+  // scale = e4m3(amax / 6): the fp32 quotient, correctly rounded, clamped at
+  // 448 and rounded to e4m3 by the unit-scale fp8 conversion, then its exact
+  // value back through the fp8 -> fp32 conversion
+  const float qs = div_by_rcp(__uint_as_float(amax << 16), 6.0f, 0x1.555556p-3f);
+  const float qc = fminf(qs, 448.0f);
+  const s16x2 cw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, qc, qc, 1.0f, false);
+  const uint32_t sc = (uint32_t)cw.x & 0xFFu;
+  const float s = __builtin_amdgcn_cvt_scalef32_f32_fp8(sc, 1.0f, 0);
   const float rs = __builtin_amdgcn_rcpf(s);
   const float xf[8] = {bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y),
                        bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
@@ -115,13 +115,53 @@ __device__ __forceinline__ void store_row_wave<kV41Fp4>(uint4 x, uint8_t* data, 
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, qf[2], qf[3], 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, qf[4], qf[5], 1.0f, 2);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, qf[6], qf[7], 1.0f, 3);
-  w = sc == 0 ? 0u : w;                            // zero scale: all codes 0
+  RowQ<kV41Fp4> q;
+  q.w = sc == 0 ? 0u : w;                          // zero scale: all codes 0
   // scale bytes: group g's code sits on lanes 2g, 2g+1; lane 8k+6 packs the
-  // bytes of groups 4k..4k+3 and the eight packing lanes store 32 B
-  const uint32_t sw = pack4_bytes_shr<2>(sc);
+  // bytes of groups 4k..4k+3
+  q.sw = pack4_bytes_shr<2>(sc);
+  return q;
+}
+
+template <int L>
+__device__ __forceinline__ void store_quantized(const RowQ<L>& q, uint4 x, uint8_t* data,
+                                                uint8_t* scale, bool write);
+
+template <>
+__device__ __forceinline__ void store_quantized<kV41>(const RowQ<kV41>& q, uint4, uint8_t* data,
+                                                      uint8_t* scale, bool write) {
   if (!write) return;
-  *(uint32_t*)(data + 4 * lane) = w;
-  if ((lane & 7) == 6) *(uint32_t*)(scale + 4 * (lane >> 3)) = sw;
+  const int lane = lane_id();
+  *(u32x2*)(data + 8 * lane) = u32x2{q.w0, q.w1};
+  if ((lane & 15) == 12) *(uint32_t*)(scale + 4 * (lane >> 4)) = q.sw;   // 4 lanes x 4 B
+}
+
+template <>
+__device__ __forceinline__ void store_quantized<kV4>(const RowQ<kV4>& q, uint4 x, uint8_t* data,
+                                                     uint8_t* scale, bool write) {
+  if (!write) return;
+  const int lane = lane_id();
+  if (lane < kRopeLane0) {
+    *(u32x2*)(data + 8 * lane) = u32x2{q.w0, q.w1};
+  } else {                                         // rope dims kept as bf16
+    st_u4(data + kNope + 16 * (lane - kRopeLane0), x);
+  }
+  if (lane == 0) *(u32x2*)scale = u32x2{q.sc0, q.sc1};
+}
+
+template <>
+__device__ __forceinline__ void store_quantized<kV41Fp4>(const RowQ<kV41Fp4>& q, uint4,
+                                                         uint8_t* data, uint8_t* scale,
+                                                         bool write) {
+  if (!write) return;
+  const int lane = lane_id();
+  *(uint32_t*)(data + 4 * lane) = q.w;
+  if ((lane & 7) == 6) *(uint32_t*)(scale + 4 * (lane >> 3)) = q.sw;     // 8 lanes x 4 B
+}
+
+template <int L>
+__device__ __forceinline__ void store_row_wave(uint4 x, uint8_t* data, uint8_t* scale, bool write) {
+  store_quantized<L>(quantize_row<L>(x), x, data, scale, write);
 }
 
 // ------------------------------------------------------------------ exact RoPE

@@ -450,3 +450,21 @@ def test_prefill_every_tile_shape(K, tile_rows, layout, ratio, slots):
             L += 1
     assert r["n_rows"] == L
     check_compress(r, layout, 8, slots_, lat)
+
+
+@pytest.mark.parametrize("layout,gsize", [("V41_FP4", 16), ("V41", 32)])
+def test_group_scale_every_amax(K, layout, gsize):
+    """every positive finite bf16 as a group's amax (its sign alternating),
+    the rest of the group random below it: scale bytes and codes equal the
+    oracle's."""
+    _say("scale every amax", layout)
+    b = spec.all_bf16()
+    b = b[(b & 0x8000) == 0]
+    rng = np.random.default_rng(330 + gsize)
+    amax = spec.bf16_value(b)
+    frac = rng.random((b.size, gsize - 1))
+    rest = spec.bf16_nearest(amax[:, None] * frac * np.where(rng.random(frac.shape) < 0.5, -1, 1))
+    lead = np.where(np.arange(b.size) % 2 == 1, b | np.uint16(0x8000), b).astype(np.uint16)
+    groups = np.concatenate([lead[:, None], rest], axis=1)
+    rows = _groups_to_rows(groups, gsize)
+    _store_and_compare(K, layout, rows)
