@@ -234,7 +234,7 @@ __device__ __forceinline__ void dest_loc(const CompressParams& p, int32_t b, int
   if (p.dcp_world > 1) {
     const int kl = p.dcp_interleave_log2;
     const uint32_t run = (uint32_t)(c >> kl);
-    const uint32_t turn = run / (uint32_t)p.dcp_world;
+    const uint32_t turn = udiv_magic(run, p.dcp_div.m, p.dcp_div.sh1, p.dcp_div.sh2);
     if (run - turn * (uint32_t)p.dcp_world != (uint32_t)p.dcp_rank) {
       loc = 0;
       err = 0;
@@ -243,6 +243,16 @@ __device__ __forceinline__ void dest_loc(const CompressParams& p, int32_t b, int
     c = ((int64_t)turn << kl) | (c & ((int64_t(1) << kl) - 1));
   }
   page_loc(p, b, c, loc, err);
+}
+
+// write a token's kv and score (this lane's 16 B of each) into pending-state
+// entry st_row
+__device__ __forceinline__ void write_state_regs(const CompressParams& p, int64_t st_row,
+                                                 uint4 kvv, uint4 scv) {
+  const int dim0 = kDimsPerLane * lane_id();
+  uint16_t* st = p.state + st_row * 2 * kDim;
+  st_u4(st + dim0, kvv);
+  st_u4(st + kDim + dim0, scv);
 }
 
 // copy a token's kv and score rows into pending-state entry st_row
@@ -516,32 +526,49 @@ __global__ __launch_bounds__(kBlock) void compress_tokens_kernel(CompressParams 
     }
     return r;
   };
+  // Pending tokens (ratio 2): an even position's token becomes the pending
+  // token of its pair, unless a later token of this call takes the same ring
+  // entry.  A token followed by the odd token of its pair is already in that
+  // row's registers (its first token) and is written from there after the
+  // row; a last token at an even position is loaded up front and written at
+  // the end.  Every ring write follows the row that reads the ring.
+  const int64_t last_pair = (P + D - 1) >> 1;
+  const bool tail = RATIO == 2 && ((P + D - 1) & 1) == 0;
+  uint4 tail_kv = make_uint4(0u, 0u, 0u, 0u), tail_sc = tail_kv;
+  if (tail) {
+    const int dim0 = kDimsPerLane * lane;
+    tail_kv = ld_u4_nt(p.kv + (t0 + D - 1) * p.kv_stride + dim0);
+    tail_sc = ld_u4_nt(p.score + (t0 + D - 1) * p.score_stride + dim0);
+  }
+  auto pend_from_row = [&](const RowJob& j, const RowIn& in) {
+    if constexpr (RATIO == 2) {
+      const int64_t q = P + (j.t1 - t0);       // the row's odd position
+      const int64_t k = (q - 1) >> 1;
+      if (!j.from_state && k + p.ring_slots > last_pair)
+        write_state_regs(p, ring_row(p, b, k), in.k0, in.s0);
+    }
+  };
   // tokens that close a row: every token (ratio 1), odd positions (ratio 2)
   const int32_t first = (RATIO == 2 && (P & 1) == 0) ? 1 : 0;
   const int32_t step = RATIO == 2 ? 2 : 1;
   for (int32_t jj = first; jj < D; jj += 2 * step) {
     const bool two = jj + step < D;
     const RowJob j0 = job(jj);
-    const RowJob j1 = two ? job(jj + step) : j0;
     if (two) {
+      const RowJob j1 = job(jj + step);
       const RowIn in0 = load_row<RATIO>(p, j0);
       const RowIn in1 = load_row<RATIO>(p, j1);
       finish_row<L, RATIO>(p, kv, w, j0, in0);
       finish_row<L, RATIO>(p, kv, w, j1, in1);
+      pend_from_row(j0, in0);
+      pend_from_row(j1, in1);
     } else {
-      finish_row<L, RATIO>(p, kv, w, j0, load_row<RATIO>(p, j0));
+      const RowIn in0 = load_row<RATIO>(p, j0);
+      finish_row<L, RATIO>(p, kv, w, j0, in0);
+      pend_from_row(j0, in0);
     }
   }
-  if constexpr (RATIO == 2) {
-    // an even position's token becomes the pending token of its pair, unless
-    // a later token of this call takes the same ring entry
-    const int64_t last_pair = (P + D - 1) >> 1;
-    for (int32_t jj = 0; jj < D; ++jj) {
-      const int64_t q = P + jj;
-      if ((q & 1) != 0 || (q >> 1) + p.ring_slots <= last_pair) continue;
-      write_state(p, ring_row(p, b, q >> 1), t0 + jj);
-    }
-  }
+  if (tail) write_state_regs(p, ring_row(p, b, last_pair), tail_kv, tail_sc);
 }
 
 template <int L, int RATIO>

@@ -209,6 +209,7 @@ int kvc_dcp_filter_ids(const int32_t* ids, int64_t T, int32_t k, int64_t ids_str
   p.page_bits = page_bits_of(page_size);
   p.num_pages = num_pages;
   p.world = world;
+  p.world_div = kvc::div_magic((uint32_t)world);
   p.rank = rank;
   p.interleave_log2 = page_bits_of(interleave);
   p.out_slots = out_slots;
@@ -316,6 +317,7 @@ int kvc_compress_store(const kvc_compress_args* a, void* stream) {
   p.draft_len = a->mode == KVC_MODE_VERIFY ? a->draft_len : 1;
   p.ring_slots = a->ring_slots > 1 ? a->ring_slots : 1;
   p.dcp_world = world;
+  p.dcp_div = kvc::div_magic((uint32_t)world);
   p.dcp_rank = world > 1 ? a->dcp_rank : 0;
   p.dcp_interleave_log2 = world > 1 ? page_bits_of(a->dcp_interleave) : 0;
   return launched(kvc::launch_compress(p, static_cast<hipStream_t>(stream)), who);

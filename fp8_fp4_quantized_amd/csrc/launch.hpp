@@ -7,6 +7,25 @@
 
 namespace kvc {
 
+// Division of a uint32 by an invariant d >= 1 as a multiply-high and shifts
+// (the round-down method for unsigned invariant divisors of Granlund and
+// Montgomery, 1994): with l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
+// q = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0), t = mulhi(m, n).
+struct DivMagic {
+  uint32_t m;
+  int32_t sh1, sh2;
+};
+
+inline DivMagic div_magic(uint32_t d) {
+  int l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  DivMagic r;
+  r.m = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+  r.sh1 = l < 1 ? l : 1;
+  r.sh2 = l > 1 ? l - 1 : 0;
+  return r;
+}
+
 struct CacheView {
   uint8_t* base;
   int64_t page_stride;
@@ -40,6 +59,7 @@ struct DcpFilterParams {
   int32_t page_bits;
   int64_t num_pages;
   int32_t world;
+  DivMagic world_div;
   int32_t rank;
   int32_t interleave_log2;
   int32_t* out_slots;
@@ -87,6 +107,7 @@ struct CompressParams {
   int32_t draft_len;           // tokens per slot in decode / verify (decode: 1)
   int32_t ring_slots;          // pending-state entries per slot (>= 1)
   int32_t dcp_world;           // context-parallel ranks (1: none)
+  DivMagic dcp_div;            // division by dcp_world
   int32_t dcp_rank;
   int32_t dcp_interleave_log2; // log2 of the rows per rank turn
   int32_t tile_log2;           // set by the launcher: log2 of rows per prefill work item

@@ -195,8 +195,8 @@ __device__ __forceinline__ uint32_t bf16_from_f64(double d) {
 // rotated value in fp64 (the products of a bf16 and an fp32 value are exact
 // there, so one rounding remains) and rounds it to bf16; the rope lanes then
 // pull the rotated pairs back.  Every lane of the wave must call this; the
-// nope lanes get x back.  fr: the position's 64 table entries.
-__device__ __forceinline__ uint4 rope_row_exact(uint4 x, const float* fr) {
+// nope lanes get x back.  f: lane k's table entry k of the row's position.
+__device__ __forceinline__ uint4 rope_row_exact(uint4 x, float f) {
   const int lane = lane_id();
   const int pair = lane >> 1;
   const int src = kRopeLane0 + (pair >> 2);
@@ -204,7 +204,6 @@ __device__ __forceinline__ uint4 rope_row_exact(uint4 x, const float* fr) {
   const uint32_t w2 = (uint32_t)__shfl((int)x.z, src), w3 = (uint32_t)__shfl((int)x.w, src);
   const int k = pair & 3;
   const uint32_t w = k == 0 ? w0 : (k == 1 ? w1 : (k == 2 ? w2 : w3));
-  const float f = fr[lane];
   const float g = dpp_f32<kDppQuadXor1>(f);     // the other entry of the pair
   const bool odd = (lane & 1) != 0;
   const double a = (double)bf16_lo(w), b = (double)bf16_hi(w);

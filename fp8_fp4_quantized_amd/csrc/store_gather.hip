@@ -42,12 +42,22 @@ __global__ __launch_bounds__(kBlock) void store_rows_kernel(StoreParams p) {
   for (int64_t i0 = wave0 * kStoreRows; i0 < p.n; i0 += nwaves * kStoreRows) {
     uint4 x[kStoreRows];
     int64_t loc[kStoreRows], pos[kStoreRows];
+    float fr[kStoreRows];
 #pragma unroll
     for (int u = 0; u < kStoreRows; ++u) {
       const int64_t i = i0 + u < p.n ? i0 + u : p.n - 1;
       x[u] = ld_u4_nt(p.rows + i * p.row_stride + kDimsPerLane * lane);
       loc[u] = ld_ro(p.out_loc + i);
       pos[u] = ROPE ? ld_ro(p.positions + i) : 0;
+    }
+    if constexpr (ROPE) {
+      // every row's table line is requested before the first row is rotated
+      // (a position outside the table reads line 0 and is not used)
+#pragma unroll
+      for (int u = 0; u < kStoreRows; ++u) {
+        const int64_t q = pos[u] >= 0 && pos[u] < p.max_pos ? pos[u] : 0;
+        fr[u] = p.freqs[q * kRope + lane];
+      }
     }
 #pragma unroll
     for (int u = 0; u < kStoreRows; ++u) {
@@ -59,7 +69,7 @@ __global__ __launch_bounds__(kBlock) void store_rows_kernel(StoreParams p) {
             raise_status(p.status, kStPosRange);
             write = false;
           } else {
-            x[u] = rope_row_exact(x[u], p.freqs + pos[u] * kRope);
+            x[u] = rope_row_exact(x[u], fr[u]);
           }
         }
       }
@@ -131,7 +141,8 @@ __global__ __launch_bounds__(kBlock) void dcp_filter_kernel(DcpFilterParams p) {
     const int64_t t = u / units_per_row;
     const int32_t part = (int32_t)(u - t * units_per_row);
     const int64_t un = u + gridDim.x;                 // next unit: its loads in flight now
-    const FilterUnit nxt = load_unit(p, un < n_units ? un : u, units_per_row, wid, lane);
+    // past the last unit: re-read unit 0, which every workgroup shares in L2
+    const FilterUnit nxt = load_unit(p, un < n_units ? un : 0, units_per_row, wid, lane);
     if (part == 0) cnt = 0;
     const int32_t req = cur.req;
     bool keep = cur.valid;
@@ -150,7 +161,7 @@ __global__ __launch_bounds__(kBlock) void dcp_filter_kernel(DcpFilterParams p) {
         uo[e] = 0;
         if (id >= 0) {
           const uint32_t run = (uint32_t)id >> kl;
-          const uint32_t turn = run / world;
+          const uint32_t turn = udiv_magic(run, p.world_div.m, p.world_div.sh1, p.world_div.sh2);
           if (run - turn * world == rank) {
             uo[e] = (int32_t)((turn << kl) | ((uint32_t)id & kmask));
             lp[e] = uo[e] >> p.page_bits;

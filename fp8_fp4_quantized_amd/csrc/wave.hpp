@@ -76,6 +76,12 @@ __device__ __forceinline__ T ld_ro(const T* p) {
   return *(const __attribute__((address_space(4))) T*)p;
 }
 
+// n / d for the DivMagic of d (launch.hpp)
+__device__ __forceinline__ uint32_t udiv_magic(uint32_t n, uint32_t m, int32_t sh1, int32_t sh2) {
+  const uint32_t t = __umulhi(m, n);
+  return (t + ((n - t) >> sh1)) >> sh2;
+}
+
 // a value the compiler may keep in a scalar register (the caller guarantees
 // it is the same on every active lane)
 __device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
