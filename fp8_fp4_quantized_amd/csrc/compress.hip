@@ -39,22 +39,31 @@ __device__ __forceinline__ void raise_status(int32_t* status, int32_t bit) {
 // One compressed row.  Token rows are indices into the projection buffer;
 // `from_state` says the pair's first token is the pending-state entry
 // `st_row` (entries counted over all slots: slot b's ring starts at entry
-// b * ring_slots).
+// b * ring_slots).  Indices are 32-bit: positions, offsets and the LDS row
+// tables are int32, cache slots are below 2^31 (num_pages * page_size is
+// checked on the host) and rings hold at most 8191 * 1024 entries;
+// addresses are formed in 64 bits where they are used.
 struct RowJob {
-  int64_t t1;             // second (or only) token of the row
-  int64_t rot_pos;        // rotary position
-  int64_t latent_idx;
-  int64_t loc;            // destination slot in the cache (0: no write)
-  int64_t st_row;
+  int32_t t1;             // second (or only) token of the row
+  int32_t rot_pos;        // rotary position
+  int32_t latent_idx;
+  int32_t loc;            // destination slot in the cache (0: no write)
+  int32_t st_row;
   int32_t loc_err;        // status bit raised instead of the write (0: none)
   bool from_state;
 };
 
+// a rotary position held in 32 bits: positions past 2^31 - 1 (beyond any
+// table) saturate, so they are reported as outside the table
+__device__ __forceinline__ int32_t sat_pos(int64_t q) {
+  return q > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)q;
+}
+
 // the pending-state entry of pair k of slot b: entry k % ring_slots of the
-// slot's ring (positions are int32, so k fits in 32 bits)
-__device__ __forceinline__ int64_t ring_row(const CompressParams& p, int32_t b, int64_t k) {
+// slot's ring
+__device__ __forceinline__ int32_t ring_row(const CompressParams& p, int32_t b, int32_t k) {
   const uint32_t R = (uint32_t)p.ring_slots;
-  return (int64_t)b * R + (R == 1 ? 0 : (uint32_t)k % R);
+  return (int32_t)((uint32_t)b * R + (R == 1 ? 0u : (uint32_t)k % R));
 }
 
 // registers of one row's inputs: this lane's 16 B of the pair's kv and score
@@ -74,18 +83,18 @@ __device__ __forceinline__ RowIn load_row(const CompressParams& p, const RowJob&
   const int lane = lane_id();
   const int dim0 = kDimsPerLane * lane;
   RowIn in;
-  in.k1 = ld_u4_nt(p.kv + j.t1 * p.kv_stride + dim0);
+  in.k1 = ld_u4_nt(p.kv + (int64_t)j.t1 * p.kv_stride + dim0);
   in.k0 = in.s0 = in.s1 = make_uint4(0u, 0u, 0u, 0u);
   if constexpr (RATIO == 2) {
-    in.s1 = ld_u4_nt(p.score + j.t1 * p.score_stride + dim0);
-    const uint16_t* st = p.state + j.st_row * 2 * kDim;
-    const uint16_t* k0 = j.from_state ? st : p.kv + (j.t1 - 1) * p.kv_stride;
-    const uint16_t* s0 = j.from_state ? st + kDim : p.score + (j.t1 - 1) * p.score_stride;
+    in.s1 = ld_u4_nt(p.score + (int64_t)j.t1 * p.score_stride + dim0);
+    const uint16_t* st = p.state + (int64_t)j.st_row * 2 * kDim;
+    const uint16_t* k0 = j.from_state ? st : p.kv + (int64_t)(j.t1 - 1) * p.kv_stride;
+    const uint16_t* s0 = j.from_state ? st + kDim : p.score + (int64_t)(j.t1 - 1) * p.score_stride;
     in.k0 = ld_u4(k0 + dim0);
     in.s0 = ld_u4(s0 + dim0);
   }
-  const int64_t rp = j.rot_pos < 0 ? 0 : (j.rot_pos >= p.max_pos ? p.max_pos - 1 : j.rot_pos);
-  in.f = p.freqs[rp * kRope + lane];
+  const int32_t rp = j.rot_pos < 0 ? 0 : (j.rot_pos >= p.max_pos ? (int32_t)p.max_pos - 1 : j.rot_pos);
+  in.f = p.freqs[(int64_t)rp * kRope + lane];
   return in;
 }
 
@@ -186,8 +195,9 @@ __device__ __forceinline__ void store_row_out(const CompressParams& p, const Pag
   const int dim0 = kDimsPerLane * lane_id();
   const bool lat_ok = j.latent_idx < p.max_out_rows;
   if (lat_ok) {
-    st_u4_nt(p.latent + j.latent_idx * p.latent_stride + dim0, o.lat);
-    if (p.prequant != nullptr) st_u4(p.prequant + j.latent_idx * p.prequant_stride + dim0, o.z);
+    st_u4_nt(p.latent + (int64_t)j.latent_idx * p.latent_stride + dim0, o.lat);
+    if (p.prequant != nullptr)
+      st_u4(p.prequant + (int64_t)j.latent_idx * p.prequant_stride + dim0, o.z);
   } else {
     raise_status(p.status, kStLatentRange);
   }
@@ -197,7 +207,7 @@ __device__ __forceinline__ void store_row_out(const CompressParams& p, const Pag
     raise_status(p.status, kStPageRange);
     write = false;
   }
-  const int64_t slot = write ? j.loc : 0;
+  const int32_t slot = write ? j.loc : 0;
   store_quantized<L>(o.q, o.z, kv.data(slot), kv.scale(slot), write);
 }
 
@@ -208,59 +218,59 @@ __device__ __forceinline__ void finish_row(const CompressParams& p, const PagedK
 }
 
 // the destination slot of row c of slot b through the page table
-__device__ __forceinline__ void page_loc(const CompressParams& p, int32_t b, int64_t c,
-                                         int64_t& loc, int32_t& err) {
+__device__ __forceinline__ void page_loc(const CompressParams& p, int32_t b, int32_t c,
+                                         int32_t& loc, int32_t& err) {
   loc = 0;
   err = 0;
-  const int64_t lp = c >> p.cache.page_bits;
+  const int32_t lp = c >> p.cache.page_bits;
   if (lp >= p.pt_stride) {
     err = kStPtRange;
     return;
   }
-  const int64_t phys = ld_ro(p.page_table + (int64_t)b * p.pt_stride + lp);
+  const int32_t phys = ld_ro(p.page_table + (int64_t)b * p.pt_stride + lp);
   if (phys < 0 || phys >= p.cache.num_pages) {
     err = kStPageRange;
     return;
   }
-  loc = (phys << p.cache.page_bits) | (c & ((int64_t(1) << p.cache.page_bits) - 1));
+  loc = (phys << p.cache.page_bits) | (c & ((1 << p.cache.page_bits) - 1));
 }
 
 // the destination of row c of slot b on this rank: with the rows dealt over
 // a decode-context-parallel group in runs of K = 2^interleave_log2, run
 // c / K belongs to rank (c / K) % world, which keeps it as its row
 // (c / (K * world)) * K + c % K; rows of other ranks are not stored (loc 0)
-__device__ __forceinline__ void dest_loc(const CompressParams& p, int32_t b, int64_t c,
-                                         int64_t& loc, int32_t& err) {
+__device__ __forceinline__ void dest_loc(const CompressParams& p, int32_t b, int32_t c,
+                                         int32_t& loc, int32_t& err) {
   if (p.dcp_world > 1) {
     const int kl = p.dcp_interleave_log2;
-    const uint32_t run = (uint32_t)(c >> kl);
+    const uint32_t run = (uint32_t)c >> kl;
     const uint32_t turn = udiv_magic(run, p.dcp_div.m, p.dcp_div.sh1, p.dcp_div.sh2);
     if (run - turn * (uint32_t)p.dcp_world != (uint32_t)p.dcp_rank) {
       loc = 0;
       err = 0;
       return;
     }
-    c = ((int64_t)turn << kl) | (c & ((int64_t(1) << kl) - 1));
+    c = (int32_t)((turn << kl) | ((uint32_t)c & ((1u << kl) - 1)));
   }
   page_loc(p, b, c, loc, err);
 }
 
 // write a token's kv and score (this lane's 16 B of each) into pending-state
 // entry st_row
-__device__ __forceinline__ void write_state_regs(const CompressParams& p, int64_t st_row,
+__device__ __forceinline__ void write_state_regs(const CompressParams& p, int32_t st_row,
                                                  uint4 kvv, uint4 scv) {
   const int dim0 = kDimsPerLane * lane_id();
-  uint16_t* st = p.state + st_row * 2 * kDim;
+  uint16_t* st = p.state + (int64_t)st_row * 2 * kDim;
   st_u4(st + dim0, kvv);
   st_u4(st + kDim + dim0, scv);
 }
 
 // copy a token's kv and score rows into pending-state entry st_row
-__device__ __forceinline__ void write_state(const CompressParams& p, int64_t st_row, int64_t tok) {
+__device__ __forceinline__ void write_state(const CompressParams& p, int32_t st_row, int32_t tok) {
   const int dim0 = kDimsPerLane * lane_id();
-  uint16_t* st = p.state + st_row * 2 * kDim;
-  const uint4 kvv = ld_u4_nt(p.kv + tok * p.kv_stride + dim0);
-  const uint4 scv = ld_u4_nt(p.score + tok * p.score_stride + dim0);
+  uint16_t* st = p.state + (int64_t)st_row * 2 * kDim;
+  const uint4 kvv = ld_u4_nt(p.kv + (int64_t)tok * p.kv_stride + dim0);
+  const uint4 scv = ld_u4_nt(p.score + (int64_t)tok * p.score_stride + dim0);
   st_u4(st + dim0, kvv);
   st_u4(st + kDim + dim0, scv);
 }
@@ -280,13 +290,16 @@ template <int RATIO>
 __device__ __forceinline__ SlotWork slot_work(int32_t n, int32_t P, int32_t tile_log2) {
   SlotWork s{0, 0, 0, false};
   if (n <= 0 || P < 0) return s;
+  // positions are int32: a slot running past 2^31 - 1 is cut there (its
+  // result is unspecified, but every index stays in range)
+  const int32_t end = (int64_t)P + n > 0x7FFFFFFF ? 0x7FFFFFFF : P + n;
   if constexpr (RATIO == 1) {
-    s.rows = n;
+    s.rows = end - P;
     s.c0 = P;
   } else {
-    s.rows = ((P + n) >> 1) - (P >> 1);      // odd positions in [P, P + n)
+    s.rows = (end >> 1) - (P >> 1);          // odd positions in [P, end)
     s.c0 = P >> 1;                           // row of the first odd position
-    s.tail = ((P + n) & 1) != 0;             // last position P + n - 1 is even
+    s.tail = (end & 1) != 0;                 // last position end - 1 is even
   }
   if (s.rows > 0) {
     s.items = ((s.c0 + s.rows - 1) >> tile_log2) - (s.c0 >> tile_log2) + 1;
@@ -346,15 +359,15 @@ __device__ void build_tables(const CompressParams& p, int32_t* item_start, int32
 // One prefill work item: the tile kt of slot b (slot data already at hand).
 template <int L, int RATIO, int kTileRows>
 __device__ __forceinline__ void run_tile(const CompressParams& p, const PagedKV<L>& kv,
-                                         const float (&w)[8], int32_t b, int64_t kt, int64_t lat0,
-                                         int64_t rows, int64_t first, int32_t n, int64_t P) {
+                                         const float (&w)[8], int32_t b, int32_t kt, int32_t lat0,
+                                         int32_t rows, int32_t first, int32_t n, int32_t P) {
   const int tl = p.tile_log2;
-  const int64_t page_mask = (int64_t(1) << p.cache.page_bits) - 1;
-  const int64_t c0 = RATIO == 1 ? P : (P >> 1);
-  const int64_t tbase = ((c0 >> tl) + kt) << tl;
-  const int64_t c_lo = c0 > tbase ? c0 : tbase;
-  const int64_t c_end = c0 + rows, t_end = tbase + (int64_t(1) << tl);
-  const int64_t c_hi = c_end < t_end ? c_end : t_end;
+  const int32_t page_mask = (1 << p.cache.page_bits) - 1;
+  const int32_t c0 = RATIO == 1 ? P : (P >> 1);
+  const int32_t tbase = ((c0 >> tl) + kt) << tl;
+  const int32_t c_lo = c0 > tbase ? c0 : tbase;
+  const int32_t c_end = c0 + rows, t_end = tbase + (1 << tl);
+  const int32_t c_hi = c_end < t_end ? c_end : t_end;
 
   if (c_lo < c_hi) {
     // all loads of the tile's rows are issued before the first row is
@@ -363,7 +376,7 @@ __device__ __forceinline__ void run_tile(const CompressParams& p, const PagedKV<
     RowIn in[kTileRows];
 #pragma unroll
     for (int r = 0; r < kTileRows; ++r) {
-      const int64_t c = c_lo + r < c_hi ? c_lo + r : c_hi - 1;
+      const int32_t c = c_lo + r < c_hi ? c_lo + r : c_hi - 1;
       j[r].st_row = 0;
       j[r].latent_idx = lat0 + (c - c0);
       if constexpr (RATIO == 1) {
@@ -371,9 +384,9 @@ __device__ __forceinline__ void run_tile(const CompressParams& p, const PagedKV<
         j[r].rot_pos = c;
         j[r].from_state = false;
       } else {
-        const int64_t q = 2 * c + 1;             // odd position closing the pair
-        j[r].t1 = first + (q - P);
-        j[r].rot_pos = q - 1;
+        const int64_t q = 2 * (int64_t)c + 1;    // odd position closing the pair
+        j[r].t1 = first + (int32_t)(q - P);
+        j[r].rot_pos = sat_pos(q - 1);
         j[r].from_state = q - 1 < P;             // first token precedes the extend
         if (j[r].from_state) j[r].st_row = ring_row(p, b, c);
       }
@@ -383,16 +396,16 @@ __device__ __forceinline__ void run_tile(const CompressParams& p, const PagedKV<
       // rows dealt over a context-parallel group: each row has its own owner
 #pragma unroll
       for (int r = 0; r < kTileRows; ++r) {
-        const int64_t c = c_lo + r < c_hi ? c_lo + r : c_hi - 1;
+        const int32_t c = c_lo + r < c_hi ? c_lo + r : c_hi - 1;
         dest_loc(p, b, c, j[r].loc, j[r].loc_err);
       }
     } else {
       // the tile's rows share one page (aligned, no larger than a page): one
       // page-table lookup, needed only when the rows are stored
-      int64_t loc0;
+      int32_t loc0;
       int32_t loc_err;
       page_loc(p, b, c_lo, loc0, loc_err);
-      const int64_t page_base = loc0 - (c_lo & page_mask);
+      const int32_t page_base = loc0 - (c_lo & page_mask);
 #pragma unroll
       for (int r = 0; r < kTileRows; ++r) {
         j[r].loc_err = loc_err;
@@ -410,7 +423,8 @@ __device__ __forceinline__ void run_tile(const CompressParams& p, const PagedKV<
     }
   }
   if constexpr (RATIO == 2) {
-    if (kt == 0 && ((P + n) & 1)) write_state(p, ring_row(p, b, (P + n - 1) >> 1), first + n - 1);
+    if (kt == 0 && (((int64_t)P + n) & 1))
+      write_state(p, ring_row(p, b, (int32_t)(((int64_t)P + n - 1) >> 1)), first + n - 1);
   }
 }
 
@@ -441,15 +455,15 @@ __global__ __launch_bounds__(kBlock) void compress_prefill_small_kernel(Compress
   }
   const float w[8] = {bf16_lo(wr.x), bf16_hi(wr.x), bf16_lo(wr.y), bf16_hi(wr.y),
                       bf16_lo(wr.z), bf16_hi(wr.z), bf16_lo(wr.w), bf16_hi(wr.w)};
-  const int64_t total = __builtin_amdgcn_readlane(inc_i, kLanes - 1);
-  const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t item = wave0; item < total; item += nwaves) {
+  const int32_t total = __builtin_amdgcn_readlane(inc_i, kLanes - 1);
+  const int32_t wave0 = uniform((int32_t)blockIdx.x * kWavesPerBlock + (int32_t)(threadIdx.x >> 6));
+  const int32_t nwaves = (int32_t)gridDim.x * kWavesPerBlock;
+  for (int32_t item = wave0; item < total; item += nwaves) {
     // slot b = number of slots whose items all come before this one
     const int32_t b = __builtin_popcountll(__ballot(inc_i <= item));
-    const int64_t kt = item - (__builtin_amdgcn_readlane(inc_i, b) - __builtin_amdgcn_readlane(sw.items, b));
-    const int64_t rows = __builtin_amdgcn_readlane(sw.rows, b);
-    const int64_t lat0 = __builtin_amdgcn_readlane(inc_r, b) - rows;
+    const int32_t kt = item - (__builtin_amdgcn_readlane(inc_i, b) - __builtin_amdgcn_readlane(sw.items, b));
+    const int32_t rows = __builtin_amdgcn_readlane(sw.rows, b);
+    const int32_t lat0 = __builtin_amdgcn_readlane(inc_r, b) - rows;
     run_tile<L, RATIO, kTileRows>(p, kv, w, b, kt, lat0, rows, __builtin_amdgcn_readlane(first, b),
                                   __builtin_amdgcn_readlane(n, b), __builtin_amdgcn_readlane(P, b));
   }
@@ -465,23 +479,23 @@ __global__ __launch_bounds__(kBlock) void compress_prefill_kernel(CompressParams
   const uint4 wr = ld_u4(p.norm_w + kDimsPerLane * lane);
   const float w[8] = {bf16_lo(wr.x), bf16_hi(wr.x), bf16_lo(wr.y), bf16_hi(wr.y),
                       bf16_lo(wr.z), bf16_hi(wr.z), bf16_lo(wr.w), bf16_hi(wr.w)};
-  const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const int32_t wave0 = uniform((int32_t)blockIdx.x * kWavesPerBlock + (int32_t)(threadIdx.x >> 6));
+  const int32_t nwaves = (int32_t)gridDim.x * kWavesPerBlock;
   const int S = p.num_slots;
 
   int32_t* item_start = tables;
   int32_t* row_start = tables + (S + 1);
   build_tables<RATIO>(p, item_start, row_start);
-  const int64_t total = uniform(item_start[S]);
+  const int32_t total = uniform(item_start[S]);
 
-  for (int64_t item = wave0; item < total; item += nwaves) {
+  for (int32_t item = wave0; item < total; item += nwaves) {
     int lo = 0, hi = S;                          // item_start[lo] <= item < item_start[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (uniform(item_start[mid]) <= item) lo = mid; else hi = mid;
     }
     const int32_t b = lo;
-    const int64_t lat0 = uniform(row_start[b]);
+    const int32_t lat0 = uniform(row_start[b]);
     run_tile<L, RATIO, kTileRows>(p, kv, w, b, item - uniform(item_start[b]), lat0,
                                   uniform(row_start[b + 1]) - lat0, ld_ro(p.offsets + b),
                                   ld_ro(p.offsets + S + b), ld_ro(p.start_pos + b));
@@ -512,17 +526,23 @@ __global__ __launch_bounds__(kBlock) void compress_tokens_kernel(CompressParams 
   auto job = [&](int32_t jj) {
     const int64_t q = P + jj;
     RowJob r;
-    r.t1 = t0 + jj;
-    r.latent_idx = t0 + jj;
+    r.t1 = (int32_t)(t0 + jj);
+    r.latent_idx = (int32_t)(t0 + jj);
     r.from_state = RATIO == 2 && jj == 0;
-    r.st_row = r.from_state ? ring_row(p, b, q >> 1) : 0;
-    r.rot_pos = RATIO == 2 ? q - 1 : q;
+    r.st_row = r.from_state ? ring_row(p, b, (int32_t)(q >> 1)) : 0;
+    r.rot_pos = sat_pos(RATIO == 2 ? q - 1 : q);
     // destination: the caller's out_loc (0 = padded row) or the page table
     if (p.out_loc != nullptr) {
       r.loc = ld_ro(p.out_loc + t0 + jj);
       r.loc_err = 0;
     } else {
-      dest_loc(p, b, RATIO == 2 ? (q >> 1) : q, r.loc, r.loc_err);
+      const int64_t c = RATIO == 2 ? (q >> 1) : q;
+      if (c > 0x7FFFFFFF) {
+        r.loc = 0;
+        r.loc_err = kStPtRange;
+      } else {
+        dest_loc(p, b, (int32_t)c, r.loc, r.loc_err);
+      }
     }
     return r;
   };
@@ -545,7 +565,7 @@ __global__ __launch_bounds__(kBlock) void compress_tokens_kernel(CompressParams 
       const int64_t q = P + (j.t1 - t0);       // the row's odd position
       const int64_t k = (q - 1) >> 1;
       if (!j.from_state && k + p.ring_slots > last_pair)
-        write_state_regs(p, ring_row(p, b, k), in.k0, in.s0);
+        write_state_regs(p, ring_row(p, b, (int32_t)k), in.k0, in.s0);
     }
   };
   // tokens that close a row: every token (ratio 1), odd positions (ratio 2)
@@ -568,7 +588,7 @@ __global__ __launch_bounds__(kBlock) void compress_tokens_kernel(CompressParams 
       pend_from_row(j0, in0);
     }
   }
-  if (tail) write_state_regs(p, ring_row(p, b, last_pair), tail_kv, tail_sc);
+  if (tail) write_state_regs(p, ring_row(p, b, (int32_t)last_pair), tail_kv, tail_sc);
 }
 
 template <int L, int RATIO>

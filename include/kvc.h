@@ -260,6 +260,10 @@ typedef struct kvc_compress_args {
   int32_t dcp_rank;           /* 0 .. dcp_world - 1 */
   int32_t dcp_interleave;     /* consecutive rows per rank turn, >= 1, divides page_size */
 } kvc_compress_args;
+/* Index ranges: token positions (start_pos + i) stay below 2^31, the rows a
+ * prefill batch emits and the token rows of a decode / verify batch (num_slots
+ * * draft_len) number fewer than 2^31.  Beyond them the results are
+ * unspecified; no access leaves the buffers the other arguments describe. */
 
 int kvc_compress_store(const kvc_compress_args* args, void* stream);
 
