@@ -166,27 +166,25 @@ __device__ __forceinline__ void store_row_wave(uint4 x, uint8_t* data, uint8_t* 
 
 // ------------------------------------------------------------------ exact RoPE
 // fp64 -> bf16, nearest even, with bf16 subnormals and overflow to infinity;
-// NaN gives 0x7FC0.  Integer rounding of the fp64 significand, so the result
-// does not depend on the float denormal mode.
+// NaN gives 0x7FC0.  Two roundings that together make one: d to fp32 by
+// round-to-odd (the hardware's nearest-even conversion, stepped back one
+// pattern when it rounded away from zero, then the last bit set when
+// inexact), then that fp32 to bf16 by nearest even on its bit pattern.  With
+// 16 more significand bits than bf16, also in the subnormal range (quantum
+// 2^-149 against 2^-133), the odd intermediate never creates a false tie, so
+// the result is d rounded once (Boldo and Melquiond, "Emulation of FMA and
+// correctly rounded sums: proved algorithms using rounding to odd", 2008).
+// Needs fp32 denormals kept by the conversions (the kernels' float mode).
+// Branch-free: every lane of a wave takes the same instructions.
 __device__ __forceinline__ uint32_t bf16_from_f64(double d) {
-  const uint64_t u = (uint64_t)__double_as_longlong(d);
-  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
-  const uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
-  if (mag > 0x7FF0000000000000ull) return 0x7FC0u;
-  const int e = (int)(mag >> 52);               // fp64 biased exponent
-  const int E = e - 1023 + 127;                 // bf16 biased exponent
-  if (E >= 255) return sign | 0x7F80u;          // >= 2^128 (or infinity)
-  const uint64_t m = (mag & 0xFFFFFFFFFFFFFull) | (e != 0 ? (1ull << 52) : 0ull);
-  // keep 8 significant bits for a normal result; a subnormal result keeps
-  // the bits at or above 2^-133
-  const int drop = 45 + (E >= 1 ? 0 : 1 - E);
-  if (drop > 60) return sign;                   // below a quarter of 2^-133
-  const uint64_t r = m >> drop;
-  const uint64_t rem = m & ((1ull << drop) - 1);
-  const uint64_t half = 1ull << (drop - 1);
-  const uint32_t up = (rem > half || (rem == half && (r & 1))) ? 1u : 0u;
-  const uint32_t out = (E >= 1 ? ((uint32_t)(E - 1) << 7) : 0u) + (uint32_t)r + up;
-  return sign | (out >= 0x7F80u ? 0x7F80u : out);
+  const float t = (float)d;                      // nearest even, may overflow to inf
+  const double back = (double)t;
+  uint32_t u = __float_as_uint(t);
+  const bool inexact = back != d;
+  u = inexact && __builtin_fabs(back) > __builtin_fabs(d) ? u - 1u : u;
+  u = inexact ? (u | 1u) : u;
+  const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return d != d ? 0x7FC0u : r;
 }
 
 // Rotate the row's 64 rope dims, (448 + 2j, 449 + 2j) by (cos, sin) =
@@ -202,8 +200,8 @@ __device__ __forceinline__ uint4 rope_row_exact(uint4 x, float f) {
   const int src = kRopeLane0 + (pair >> 2);
   const uint32_t w0 = (uint32_t)__shfl((int)x.x, src), w1 = (uint32_t)__shfl((int)x.y, src);
   const uint32_t w2 = (uint32_t)__shfl((int)x.z, src), w3 = (uint32_t)__shfl((int)x.w, src);
-  const int k = pair & 3;
-  const uint32_t w = k == 0 ? w0 : (k == 1 ? w1 : (k == 2 ? w2 : w3));
+  const bool k1 = (pair & 1) != 0, k2 = (pair & 2) != 0;   // word pair & 3 of the rope lane
+  const uint32_t w = k2 ? (k1 ? w3 : w2) : (k1 ? w1 : w0);
   const float g = dpp_f32<kDppQuadXor1>(f);     // the other entry of the pair
   const bool odd = (lane & 1) != 0;
   const double a = (double)bf16_lo(w), b = (double)bf16_hi(w);

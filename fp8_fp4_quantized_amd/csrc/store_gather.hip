@@ -64,13 +64,12 @@ __global__ __launch_bounds__(kBlock) void store_rows_kernel(StoreParams p) {
       if (i0 + u >= p.n) break;
       bool write = loc[u] != 0;
       if constexpr (ROPE) {
-        if (write) {
-          if (pos[u] < 0 || pos[u] >= p.max_pos) {
-            raise_status(p.status, kStPosRange);
-            write = false;
-          } else {
-            x[u] = rope_row_exact(x[u], fr[u]);
-          }
+        // rotated whatever the row (a row with no valid position is not
+        // stored), so the table loads above stay ahead of every row
+        x[u] = rope_row_exact(x[u], fr[u]);
+        if (write && (pos[u] < 0 || pos[u] >= p.max_pos)) {
+          raise_status(p.status, kStPosRange);
+          write = false;
         }
       }
       if (write && !kv.valid(loc[u])) {

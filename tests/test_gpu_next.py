@@ -261,6 +261,36 @@ def test_rope_store_c2_size(K):
     assert st == 0 and np.array_equal(host(dc), hc)
 
 
+def test_rope_store_every_magnitude(K):
+    """V4 keeps the rotated rope dims as bf16, so its bytes show the fp64 ->
+    bf16 rounding directly: rope dims drawn from every bf16 bit pattern
+    (subnormals, the largest finite values, infinities, NaNs) meet subnormal
+    and zero results, overflow to infinity and NaN; bytes equal the
+    oracle's."""
+    _say("rope store every magnitude")
+    c = W.rope_store_case(262, [4096, 3000], page_size=64, max_pos=4096, pad_frac=0.0)
+    rows = c["rows"].copy()
+    rng = np.random.default_rng(263)
+    n = rows.shape[0]
+    pat = rng.integers(0, 1 << 16, size=(n, 64)).astype(np.uint16)
+    # a third of the rows keep any pattern, a third get exponents 0..8 (bf16
+    # subnormal and zero results), a third exponents 248..254 (overflow)
+    mode = rng.integers(0, 3, size=(n, 1))
+    expo = np.where(mode == 1, rng.integers(0, 9, size=(n, 64)), rng.integers(248, 255, size=(n, 64)))
+    shaped = (pat & 0x807F) | (expo.astype(np.uint16) << 7)
+    rows[:, 448:] = np.where(mode == 0, pat, shaped).astype(np.uint16)
+    rb = oracle.layout_bytes("V4")[2]
+    stride = -(-64 * rb // 16) * 16
+    hc = np.zeros((c["num_pages"], stride), np.uint8)
+    dc = dev(hc)
+    _, st = oracle.store_rows_rope(hc, "V4", 64, rows, c["positions"], c["freqs"], c["out_loc"])
+    K.kvc_store_rows_rope(K.Cache(dc, "V4", 64), dev(rows), dev(c["positions"]), dev(c["freqs"]),
+                          dev(c["out_loc"]))
+    torch.cuda.synchronize()
+    got = host(dc)
+    assert st == 0 and np.array_equal(got, hc)
+
+
 # ================================================================= graph capture
 def test_prefill_compress_graph_replay(K):
     """The prefill compressor captured once in a graph, its offsets, start
