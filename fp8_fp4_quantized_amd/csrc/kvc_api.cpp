@@ -192,6 +192,8 @@ int kvc_dcp_filter_ids(const int32_t* ids, int64_t T, int32_t k, int64_t ids_str
     return fail(KVC_EINVAL, "%s: NULL token_to_req or out_lens", who);
   if (k > 0 && (ids == nullptr || out_slots == nullptr || ids_stride < k || out_stride < k))
     return fail(KVC_EINVAL, "%s: NULL ids or out_slots, or a row stride below k", who);
+  if (k > 0 && ((uintptr_t)out_slots & 3u) != 0)
+    return fail(KVC_EINVAL, "%s: out_slots is not 4-byte aligned", who);
   if (n_req < 0 || (n_req > 0 && (block_table == nullptr || bt_stride < 1)))
     return fail(KVC_EINVAL, "%s: n_req < 0, or no block table", who);
   if (num_pages < 1 || num_pages > ((int64_t)1 << 31) / page_size)
@@ -210,6 +212,11 @@ int kvc_dcp_filter_ids(const int32_t* ids, int64_t T, int32_t k, int64_t ids_str
   p.num_pages = num_pages;
   p.world = world;
   p.world_div = kvc::div_magic((uint32_t)world);
+  p.world_log2 = -1;
+  if ((world & (world - 1)) == 0) {
+    p.world_log2 = 0;
+    while ((1 << p.world_log2) < world) ++p.world_log2;
+  }
   p.rank = rank;
   p.interleave_log2 = page_bits_of(interleave);
   p.out_slots = out_slots;

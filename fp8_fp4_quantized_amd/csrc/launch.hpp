@@ -60,6 +60,7 @@ struct DcpFilterParams {
   int64_t num_pages;
   int32_t world;
   DivMagic world_div;
+  int32_t world_log2;          // log2(world) for a power of two, else -1
   int32_t rank;
   int32_t interleave_log2;
   int32_t* out_slots;

@@ -83,137 +83,121 @@ __global__ __launch_bounds__(kBlock) void store_rows_kernel(StoreParams p) {
 }
 
 // ------------------------------------------------------------------ DCP ids
-// Persistent workgroups walk work units of 2048 ids (a row of k ids is
-// ceil(k / 2048) units, taken in order by one workgroup).  Wave w of a
-// workgroup takes ids [512 w, 512 w + 512) of the unit, 64 consecutive ids
-// per load so every load is one contiguous 256 B.  An id's place among the
-// kept ones is its lane count in the chunk's ballot, plus the chunks before
-// it in the wave, plus the earlier waves (through LDS), plus the row's
-// earlier units.  The ids of the next unit are loaded before the current one
-// is processed, so their latency overlaps its page-table reads and stores.
-constexpr int kFilterChunks = 8;                          // 64-id loads per lane
-constexpr int kFilterUnit = kBlock * kFilterChunks;       // 2048 ids
+// One wave per row of ids, no LDS and no barrier.  A pass takes 2048 ids of
+// the row, 32 per lane: all 32 loads are issued together, then the owner
+// test, then all 32 page-table loads together, then, 64 ids at a time in the
+// row's order, a ballot gives each kept id its place after the ones already
+// kept.  A row's tail of -1 goes out in 16-byte stores.  The kernel is bound
+// by its per-id arithmetic, which is kept short: a bit-field extract and a
+// bit-field insert for a power-of-two group, no clamping on full passes, one
+// unsigned test for "kept and inside the page table", status bits gathered
+// through ballots.
+constexpr int kFilterChunks = 32;                          // 64-id loads per lane and pass
+constexpr int kFilterPass = kLanes * kFilterChunks;        // 2048 ids
 
-struct FilterUnit {
-  int32_t v[kFilterChunks];   // this lane's ids (-1 past the row)
-  int32_t req;                // the row's request
-  bool valid;                 // the row is not a padding token
-};
-
-// the ids and row data of work unit u, loaded ahead of their use
-__device__ __forceinline__ FilterUnit load_unit(const DcpFilterParams& p, int64_t u,
-                                                int32_t units_per_row, int wid, int lane) {
-  FilterUnit r;
-  const int64_t t = u / units_per_row;
-  const int32_t s0 = (int32_t)(u - t * units_per_row) * kFilterUnit;
-  r.valid = p.valid == nullptr || ld_ro(p.valid + t) != 0;
-  r.req = ld_ro(p.token_to_req + t);
-  if (p.k == 0) {                                         // no ids: nothing to read
-#pragma unroll
-    for (int e = 0; e < kFilterChunks; ++e) r.v[e] = -1;
-    return r;
-  }
-  const int32_t* row = p.ids + t * p.ids_stride;
-#pragma unroll
-  for (int e = 0; e < kFilterChunks; ++e) {
-    const int32_t i = s0 + kLanes * (kFilterChunks * wid + e) + lane;
-    const int32_t v = __builtin_nontemporal_load(row + (i < p.k ? i : p.k - 1));
-    r.v[e] = i < p.k ? v : -1;
-  }
-  return r;
-}
-
+template <bool POW2>
 __global__ __launch_bounds__(kBlock) void dcp_filter_kernel(DcpFilterParams p) {
-  __shared__ int32_t wave_cnt[2][kWavesPerBlock];
-  const int lane = lane_id(), wid = threadIdx.x >> 6;
-  const int kl = p.interleave_log2;
-  const uint32_t kmask = (1u << kl) - 1, pmask = (1u << p.page_bits) - 1;
+  const int lane = lane_id();
+  const int kl = p.interleave_log2, wl = p.world_log2, pb = p.page_bits;
+  const uint32_t kmask = (1u << kl) - 1, pmask = (1u << pb) - 1;
   const uint32_t world = (uint32_t)p.world, rank = (uint32_t)p.rank;
-  const int32_t units_per_row = p.k > 0 ? (p.k + kFilterUnit - 1) / kFilterUnit : 1;
-  const int64_t n_units = p.T * units_per_row;
-  int64_t u = blockIdx.x;
-  if (u >= n_units) return;
-  FilterUnit cur = load_unit(p, u, units_per_row, wid, lane);
-  int32_t cnt = 0;                                    // kept so far in the row
-  int parity = 0;                                     // LDS buffer of the next scan
-  for (; u < n_units; u += gridDim.x) {
-    const int64_t t = u / units_per_row;
-    const int32_t part = (int32_t)(u - t * units_per_row);
-    const int64_t un = u + gridDim.x;                 // next unit: its loads in flight now
-    // past the last unit: re-read unit 0, which every workgroup shares in L2
-    const FilterUnit nxt = load_unit(p, un < n_units ? un : 0, units_per_row, wid, lane);
-    if (part == 0) cnt = 0;
-    const int32_t req = cur.req;
-    bool keep = cur.valid;
+  // the page index of a kept id is below 2^(31 - pb); a row index of -1
+  // (not kept) shifts to 2^(32 - pb) - 1, at or past this bound
+  const uint32_t lim = 1u << (31 - pb);
+  const uint32_t bts = p.bt_stride < (int64_t)lim ? (uint32_t)p.bt_stride : lim;
+  const uint32_t npg = (uint32_t)(p.num_pages < 0x7FFFFFFF ? p.num_pages : 0x7FFFFFFF);
+  const int32_t k = p.k;
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  for (int64_t t = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)); t < p.T;
+       t += nwaves) {
+    int32_t* out = p.out_slots + t * p.out_stride;
+    const int32_t req = ld_ro(p.token_to_req + t);
+    bool keep = p.valid == nullptr || ld_ro(p.valid + t) != 0;
+    uint32_t bad = 0;                                     // status bits of the row
     if (keep && (req < 0 || req >= p.n_req)) {
-      if (part == 0 && threadIdx.x == 0 && p.status != nullptr) atomicOr(p.status, kStReqRange);
+      bad = kStReqRange;
       keep = false;
     }
-    int32_t* out = p.out_slots + t * p.out_stride;
-    if (keep && p.k > 0) {
+    int32_t cnt = 0;                                      // kept so far in the row
+    if (keep && k > 0) {
+      const int32_t* row = p.ids + t * p.ids_stride;
       const int32_t* bt = p.block_table + (int64_t)req * p.bt_stride;
-      int32_t lp[kFilterChunks], uo[kFilterChunks], pg[kFilterChunks];
+      for (int32_t s0 = 0; s0 < k; s0 += kFilterPass) {
+        int32_t v[kFilterChunks];
+        if (s0 + kFilterPass <= k) {
+          const int32_t* src = row + s0 + lane;
 #pragma unroll
-      for (int e = 0; e < kFilterChunks; ++e) {
-        const int32_t id = cur.v[e];
-        lp[e] = -1;
-        uo[e] = 0;
-        if (id >= 0) {
-          const uint32_t run = (uint32_t)id >> kl;
-          const uint32_t turn = udiv_magic(run, p.world_div.m, p.world_div.sh1, p.world_div.sh2);
-          if (run - turn * world == rank) {
-            uo[e] = (int32_t)((turn << kl) | ((uint32_t)id & kmask));
-            lp[e] = uo[e] >> p.page_bits;
+          for (int e = 0; e < kFilterChunks; ++e) v[e] = __builtin_nontemporal_load(src + kLanes * e);
+        } else {
+          // ids past the row read its last id and are not kept
+#pragma unroll
+          for (int e = 0; e < kFilterChunks; ++e) {
+            const int32_t i = s0 + kLanes * e + lane;
+            const int32_t x = __builtin_nontemporal_load(row + (i < k ? i : k - 1));
+            v[e] = i < k ? x : -1;
           }
         }
-      }
+        // owner test: v becomes this rank's row index, or -1
 #pragma unroll
-      for (int e = 0; e < kFilterChunks; ++e)
-        pg[e] = bt[lp[e] >= 0 && lp[e] < p.bt_stride ? lp[e] : 0];
-      int32_t slot[kFilterChunks], bad = 0, wave_total = 0;
-      uint64_t m[kFilterChunks];
-#pragma unroll
-      for (int e = 0; e < kFilterChunks; ++e) {
-        slot[e] = -1;
-        if (lp[e] >= 0) {
-          if (lp[e] >= p.bt_stride) {
-            bad |= kStPtRange;
-          } else if (pg[e] < 0 || pg[e] >= p.num_pages) {
-            bad |= kStPageRange;
+        for (int e = 0; e < kFilterChunks; ++e) {
+          const uint32_t id = (uint32_t)v[e];
+          uint32_t owner, uo;
+          if constexpr (POW2) {
+            owner = __builtin_amdgcn_ubfe(id, kl, wl);            // (id / K) % world
+            uo = (id & kmask) | ((id >> wl) & ~kmask);            // (id / (K world)) K + id % K
           } else {
-            slot[e] = (pg[e] << p.page_bits) | (int32_t)((uint32_t)uo[e] & pmask);
+            const uint32_t run = id >> kl;
+            const uint32_t turn = udiv_magic(run, p.world_div.m, p.world_div.sh1, p.world_div.sh2);
+            owner = run - turn * world;
+            uo = (turn << kl) | (id & kmask);
           }
+          v[e] = v[e] >= 0 && owner == rank ? (int32_t)uo : -1;
+          // the later tests read v itself (as lane masks, a pass of them
+          // would overflow the scalar registers)
+          asm volatile("" : "+v"(v[e]));
         }
-        m[e] = __ballot(slot[e] >= 0);
-        wave_total += (int32_t)__builtin_popcountll(m[e]);
-      }
-      if (bad != 0 && p.status != nullptr) atomicOr(p.status, bad);
-      if (lane == 0) wave_cnt[parity][wid] = wave_total;
-      __syncthreads();
-      int32_t before = 0, total = 0;
+        // page-table entries (an id not kept, or past the table, reads entry 0)
+        int32_t pg[kFilterChunks];
 #pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w) {
-        const int32_t c = wave_cnt[parity][w];
-        before += w < wid ? c : 0;
-        total += c;
-      }
-      int32_t off = cnt + before;
+        for (int e = 0; e < kFilterChunks; ++e) {
+          const uint32_t lp = (uint32_t)v[e] >> pb;
+          pg[e] = bt[lp < bts ? lp : 0u];
+        }
+        // slots, in the row's order.  A kept id whose page index lies past
+        // the table, or whose page is out of range, is dropped; the status
+        // bits are worked out only for a chunk that drops one.
 #pragma unroll
-      for (int e = 0; e < kFilterChunks; ++e) {
-        const int32_t pos = (int32_t)__builtin_amdgcn_mbcnt_hi(
-            (uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], 0u));
-        if (slot[e] >= 0) out[off + pos] = slot[e];
-        off += (int32_t)__builtin_popcountll(m[e]);
+        for (int e = 0; e < kFilterChunks; ++e) {
+          const uint32_t lp = (uint32_t)v[e] >> pb;
+          const int32_t q = lp < bts ? pg[e] : -1;
+          const bool ok = (uint32_t)q < npg;
+          const uint64_t m = __ballot(ok);
+          if (m != __ballot(v[e] >= 0)) {
+            if (__ballot(v[e] >= 0 && lp >= bts) != 0) bad |= kStPtRange;
+            if (__ballot(lp < bts && (uint32_t)pg[e] >= npg) != 0) bad |= kStPageRange;
+          }
+          const int32_t slot = (int32_t)(((uint32_t)pg[e] << pb) | ((uint32_t)v[e] & pmask));
+          const int32_t pos = (int32_t)__builtin_amdgcn_mbcnt_hi(
+              (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          int32_t* const ob = out + cnt;                  // uniform base, lane offset
+          if (ok) ob[(uint32_t)pos] = slot;
+          cnt += (int32_t)__builtin_popcountll(m);
+        }
       }
-      cnt += total;
-      parity ^= 1;        // the next scan writes the other buffer: a wave that
-                          // reaches it has left this one's reads behind
     }
-    if (part == units_per_row - 1) {                  // the row is complete
-      for (int32_t i = cnt + (int32_t)threadIdx.x; i < p.k; i += kBlock) out[i] = -1;
-      if (threadIdx.x == 0) p.out_lens[t] = cnt;
+    if (bad != 0 && lane == 0 && p.status != nullptr) atomicOr(p.status, (int32_t)bad);
+    // -1 over [cnt, k): up to 3 single ids to a 16-byte boundary, 16-byte
+    // stores, the last up to 3 ids
+    if (k > 0) {
+      const int32_t head = (int32_t)(((16u - ((uint32_t)(uintptr_t)(out + cnt) & 15u)) & 15u) >> 2);
+      const int32_t a0 = cnt + head < k ? cnt + head : k;
+      if (lane < a0 - cnt) out[cnt + lane] = -1;
+      const int32_t a1 = a0 + ((k - a0) & ~3);
+      for (int32_t i = a0 + 4 * lane; i < a1; i += 4 * kLanes)
+        *(int4*)(out + i) = make_int4(-1, -1, -1, -1);
+      if (lane < k - a1) out[a1 + lane] = -1;
     }
-    cur = nxt;
+    if (lane == 0) p.out_lens[t] = cnt;
   }
 }
 
@@ -382,9 +366,10 @@ hipError_t launch_store_rows(const StoreParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_dcp_filter(const DcpFilterParams& p, hipStream_t stream) {
-  // persistent: six workgroups per compute unit (measured best of 512..4096)
-  const int64_t units = p.T * (p.k > 0 ? (p.k + kFilterUnit - 1) / kFilterUnit : 1);
-  return launch(dcp_filter_kernel, grid_for(units, 1, 1536), p, stream);
+  // one wave per row (rows past the grid's waves take further turns)
+  const int blocks = grid_for(p.T, kWavesPerBlock, 1 << 20);
+  return p.world_log2 >= 0 ? launch(dcp_filter_kernel<true>, blocks, p, stream)
+                           : launch(dcp_filter_kernel<false>, blocks, p, stream);
 }
 
 hipError_t launch_dequant_gather(const GatherParams& p, hipStream_t stream) {

@@ -304,8 +304,8 @@ int kvc_dequant_gather(const kvc_cache* cache, const int32_t* page_table, int64_
  *                row (count 0) with KVC_STATUS_REQ_RANGE
  *   block_table  device int32 [n_req, bt_stride]: this rank's pages
  *   valid        device int32 [T] or NULL; 0 = a padding token: count 0
- *   out_slots    device int32, out_stride >= k; must not overlap ids (may be
- *                NULL when k = 0)
+ *   out_slots    device int32, 4-byte aligned, out_stride >= k; must not
+ *                overlap ids (may be NULL when k = 0)
  *   out_lens     device int32 [T]
  * A page index >= bt_stride (KVC_STATUS_PT_RANGE) or a page < 0 or >=
  * num_pages (KVC_STATUS_PAGE_RANGE) drops that id.  world = 1 (rank 0) maps

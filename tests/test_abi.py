@@ -123,7 +123,7 @@ def test_dcp_filter_argument_checks(kvc):
                dict(rank=2), dict(rank=-1), dict(inter=0), dict(inter=3), dict(inter=128),
                dict(t2r=None), dict(out=None), dict(lens=None), dict(ids_stride=7),
                dict(out_stride=4), dict(n_req=-1), dict(bt=None), dict(bt_stride=0),
-               dict(num_pages=0), dict(num_pages=1 << 30)):
+               dict(num_pages=0), dict(num_pages=1 << 30), dict(out=FAKE + 2)):
         assert call(**kw) == kvc.KVC_EINVAL, kw
         assert kvc.kvc_last_error()
 

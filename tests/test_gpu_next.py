@@ -194,11 +194,14 @@ def _filter(K, c, world, rank, interleave, k=None, valid=True):
 
 
 @pytest.mark.parametrize("world,interleave,k", [(1, 1, 64), (2, 1, 100), (4, 4, 2048),
-                                                 (3, 2, 7), (8, 16, 513)])
+                                                 (3, 2, 7), (8, 16, 513), (4, 2, 4100),
+                                                 (6, 4, 2100)])
 def test_dcp_filter_ids(K, world, interleave, k):
+    """every rank's slots and counts equal the oracle's; rows of one or more
+    2048-id passes, full and partial, power-of-two groups and others."""
     _say("dcp filter", world, interleave, k)
-    c = W.dcp_ids_case(240 + world, T=300, k=k, n_req=7, max_rows=3000, world=world,
-                       page_size=64)
+    c = W.dcp_ids_case(240 + world, T=300, k=k, n_req=7, max_rows=max(3000, 2 * k),
+                       world=world, page_size=64)
     total = 0
     for rank in range(world):
         (ws, wl, wst), (gs, gl, gst) = _filter(K, c, world, rank, interleave)
@@ -220,6 +223,11 @@ def test_dcp_filter_edges(K):
     assert wst & oracle.ST_REQ_RANGE and wst & oracle.ST_PAGE_RANGE
     (ws, wl, wst), (gs, gl, gst) = _filter(K, c, 2, 0, 2, k=0)
     assert gs.shape[1] == 0 and np.all(gl == 0)
+    # a block table two pages wide: ids past it are dropped with PT_RANGE
+    c["block_tables"] = [np.ascontiguousarray(b[:, :2]) for b in c["block_tables"]]
+    (ws, wl, wst), (gs, gl, gst) = _filter(K, c, 2, 1, 1, valid=False)
+    assert np.array_equal(gl, wl) and np.array_equal(gs, ws) and gst == wst
+    assert wst & oracle.ST_PT_RANGE
 
 
 # ================================================================= RoPE store
