@@ -507,13 +507,17 @@ __global__ __launch_bounds__(kBlock) void compress_prefill_kernel(CompressParams
 // at an odd position pools with the previous draft token, or for the first
 // token with the ring entry an earlier call left; the ring entries are
 // written after every row of the slot has read its inputs.
-template <int L, int RATIO>
+template <int L, int RATIO, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void compress_tokens_kernel(CompressParams p) {
   const PagedKV<L> kv{p.cache.base, p.cache.page_stride, p.cache.num_pages, p.cache.page_bits};
   const int lane = lane_id();
-  const int64_t b64 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  if (b64 >= p.num_slots) return;
-  const int32_t b = (int32_t)b64;
+  // SPLIT: wave r of a slot takes the slot's row r alone (and wave 0 the
+  // last pending token); otherwise one wave takes all of the slot's rows
+  const int32_t per_slot = SPLIT ? (RATIO == 2 ? (p.draft_len + 1) >> 1 : p.draft_len) : 1;
+  const int64_t w64 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  if (w64 >= (int64_t)p.num_slots * per_slot) return;
+  const int32_t b = (int32_t)(w64 / per_slot);
+  const int32_t r_only = (int32_t)(w64 - (int64_t)b * per_slot);
   const int64_t P = ld_ro(p.start_pos + b);
   if (P < 0) return;
   const int32_t D = p.draft_len;
@@ -553,7 +557,7 @@ __global__ __launch_bounds__(kBlock) void compress_tokens_kernel(CompressParams 
   // row; a last token at an even position is loaded up front and written at
   // the end.  Every ring write follows the row that reads the ring.
   const int64_t last_pair = (P + D - 1) >> 1;
-  const bool tail = RATIO == 2 && ((P + D - 1) & 1) == 0;
+  const bool tail = RATIO == 2 && ((P + D - 1) & 1) == 0 && (!SPLIT || r_only == 0);
   uint4 tail_kv = make_uint4(0u, 0u, 0u, 0u), tail_sc = tail_kv;
   if (tail) {
     const int dim0 = kDimsPerLane * lane;
@@ -571,6 +575,19 @@ __global__ __launch_bounds__(kBlock) void compress_tokens_kernel(CompressParams 
   // tokens that close a row: every token (ratio 1), odd positions (ratio 2)
   const int32_t first = (RATIO == 2 && (P & 1) == 0) ? 1 : 0;
   const int32_t step = RATIO == 2 ? 2 : 1;
+  if constexpr (SPLIT) {
+    // this wave's row alone: with more ring entries than pairs in a call,
+    // no other row's ring write can touch the entry the first row reads
+    const int32_t jj = first + step * r_only;
+    if (jj < D) {
+      const RowJob j0 = job(jj);
+      const RowIn in0 = load_row<RATIO>(p, j0);
+      finish_row<L, RATIO>(p, kv, w, j0, in0);
+      pend_from_row(j0, in0);
+    }
+    if (tail) write_state_regs(p, ring_row(p, b, (int32_t)last_pair), tail_kv, tail_sc);
+    return;
+  }
   for (int32_t jj = first; jj < D; jj += 2 * step) {
     const bool two = jj + step < D;
     const RowJob j0 = job(jj);
@@ -617,8 +634,17 @@ hipError_t launch_one(const CompressParams& p, hipStream_t stream) {
     }
 #undef KVC_PREFILL_LAUNCH
   } else {
-    const int blocks = (p.num_slots + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((compress_tokens_kernel<L, RATIO>), dim3(blocks), dim3(kBlock), 0, stream, p);
+    // rows of a slot in waves of their own when the ring has more entries
+    // than a call's pairs (ratio 2) -- the rows are then independent
+    const bool split = p.draft_len > 1 && (RATIO == 1 || 2 * p.ring_slots > p.draft_len);
+    const int64_t per_slot = split ? (RATIO == 2 ? (p.draft_len + 1) / 2 : p.draft_len) : 1;
+    const int blocks = (int)(((int64_t)p.num_slots * per_slot + kWavesPerBlock - 1) / kWavesPerBlock);
+    if (split)
+      hipLaunchKernelGGL((compress_tokens_kernel<L, RATIO, true>), dim3(blocks), dim3(kBlock), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((compress_tokens_kernel<L, RATIO, false>), dim3(blocks), dim3(kBlock), 0,
+                         stream, p);
   }
   return hipGetLastError();
 }
