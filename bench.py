@@ -205,6 +205,45 @@ def measure_next_rows(kvc, W, d, dev, stream):
     return res
 
 
+def measure_reuse(kvc, cache, pt, idsets, outs, stream, layers: int, forwards: int = 20):
+    """The C4 gather read by `layers` consumer layers of one forward pass:
+    through the reuse head (one gather, then hits that launch nothing) and
+    as fresh gathers.  Each forward uses the next id list, so its one gather
+    is as cold as the bench's."""
+    import torch
+    buf = kvc.KVBuf()
+
+    def fwd_reuse(f):
+        buf.begin_forward()
+        return sum(int(buf.kvc_dequant_gather_reuse(cache, pt, idsets[f % 4], outs[f % 3]))
+                   for _ in range(layers))
+
+    def fwd_fresh(f):
+        for _ in range(layers):
+            kvc.kvc_dequant_gather(cache, pt, idsets[f % 4], outs[f % 3])
+        return 0
+
+    res = {"layers": layers, "forwards": forwards}
+    for name, fn in (("fresh", fwd_fresh), ("reuse", fwd_reuse)):
+        fn(0)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hits = 0
+        t = time.perf_counter()
+        a.record(stream)
+        for f in range(1, forwards + 1):
+            hits += fn(f)
+        b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t
+        res[f"{name}_us_per_forward"] = a.elapsed_time(b) * 1e3 / forwards
+        res[f"{name}_wall_us_per_forward"] = wall * 1e6 / forwards
+        if name == "reuse":
+            res["hits_per_forward"] = hits / forwards
+    res["speedup"] = res["fresh_us_per_forward"] / res["reuse_us_per_forward"]
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,7 +251,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true",
-                    help="skip the verify / RoPE-store / DCP-filter / graph-replay measurements")
+                    help="skip the verify / RoPE-store / DCP-filter / graph-replay / reuse measurements")
     ap.add_argument("--gather-blocks", type=int, default=0)
     ap.add_argument("--compress-blocks", type=int, default=0)
     ap.add_argument("--compress-tile-rows", type=int, default=0)
@@ -374,6 +413,8 @@ def main() -> int:
 
     if not args.no_next_rows:
         out["next_rows"] = measure_next_rows(kvc, W, d, dev, stream)
+        out["next_rows"]["gather_reuse_c4_8_layers"] = measure_reuse(
+            kvc, g_cache, g_pt, g_idsets, g_outs, stream, layers=8)
 
     # ---------------------------------------------------------------- oracle
     if not args.no_cpu_baseline:
