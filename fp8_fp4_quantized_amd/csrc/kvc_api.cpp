@@ -271,6 +271,9 @@ int kvc_compress_store(const kvc_compress_args* a, void* stream) {
                 a->dcp_interleave, a->cache.page_size);
   if (a->num_slots < 0) return fail(KVC_EINVAL, "%s: num_slots < 0", who);
   if (a->num_slots == 0) return ok();
+  if (a->mode == KVC_MODE_VERIFY && (int64_t)a->num_slots * a->draft_len > 0x7FFFFFFF)
+    return fail(KVC_EINVAL, "%s: num_slots * draft_len must be below 2^31 (token indices are int32)",
+                who);
   if (a->mode == KVC_MODE_PREFILL && a->num_slots > kvc::max_prefill_slots())
     return fail(KVC_EINVAL, "%s: prefill num_slots %d > %d", who, a->num_slots, kvc::max_prefill_slots());
   if (a->kv == nullptr || !aligned16(a->kv) || !row_stride_ok(a->kv_stride))

@@ -90,8 +90,8 @@ __global__ __launch_bounds__(kBlock) void store_rows_kernel(StoreParams p) {
 // kept.  A row's tail of -1 goes out in 16-byte stores.  The kernel is bound
 // by its per-id arithmetic, which is kept short: a bit-field extract and a
 // bit-field insert for a power-of-two group, no clamping on full passes, one
-// unsigned test for "kept and inside the page table", status bits gathered
-// through ballots.
+// unsigned test for "kept and inside the page table", status bits worked out
+// only for a chunk that drops an id.
 constexpr int kFilterChunks = 32;                          // 64-id loads per lane and pass
 constexpr int kFilterPass = kLanes * kFilterChunks;        // 2048 ids
 

@@ -262,8 +262,9 @@ typedef struct kvc_compress_args {
 } kvc_compress_args;
 /* Index ranges: token positions (start_pos + i) stay below 2^31, the rows a
  * prefill batch emits and the token rows of a decode / verify batch (num_slots
- * * draft_len) number fewer than 2^31.  Beyond them the results are
- * unspecified; no access leaves the buffers the other arguments describe. */
+ * * draft_len) number fewer than 2^31 (a verify batch past that is rejected
+ * with KVC_EINVAL).  Beyond them the results are unspecified; no access
+ * leaves the buffers the other arguments describe. */
 
 int kvc_compress_store(const kvc_compress_args* args, void* stream);
 

@@ -164,6 +164,7 @@ def test_compress_argument_checks(kvc):
     assert L.kvc_compress_store(C.byref(a), None) == kvc.KVC_EINVAL
     # verify draft length, ring size and the context-parallel group
     for kw in (dict(mode=kvc.MODE_VERIFY, draft_len=0), dict(mode=kvc.MODE_VERIFY, draft_len=65),
+               dict(mode=kvc.MODE_VERIFY, draft_len=64, num_slots=1 << 25),
                dict(ring_slots=-1), dict(ring_slots=1025), dict(dcp_world=-1),
                dict(dcp_world=2, dcp_rank=2, dcp_interleave=1),
                dict(dcp_world=2, dcp_rank=-1, dcp_interleave=1),
