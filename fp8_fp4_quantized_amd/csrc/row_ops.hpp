@@ -31,9 +31,6 @@ __device__ __forceinline__ void st_u4_nt(void* p, uint4 v) {
   __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4*)p);
 }
 
-// byte k of a word
-__device__ __forceinline__ uint32_t byte_of(uint32_t w, int k) { return (w >> (8 * k)) & 0xFFu; }
-
 // Gather the scale byte held by lane `stride * g` (g = 0 .. 4*W-1) into W
 // dwords, byte g of the result in byte g % 4 of dword g / 4.  Uses
 // v_readlane, so the result is wave-uniform.
