@@ -4,19 +4,22 @@
 // and score rows (16 B per lane each), pools them with a per-dim softmax over
 // the two scores (ratio 2), RMS-normalises over the 512 dims (one wave sum),
 // writes the pre-RoPE latent, rotates the 64 rope dims (lanes 56..63, four
-// pairs per lane, no cross-lane traffic), rounds to bf16 and quantizes the row
+// pairs per lane; the table entries reach them by lane shuffles), rounds to
+// bf16 and quantizes the row
 // into its paged slot.  (sglang PR #39652 "dsv4.1: compression, KV I/O, and
 // metadata kernels", Summary and Review; sglang PR #46230, summary.)
 //
-// Prefill batches are ragged: each workgroup turns the int32 [2, S] extend
-// offsets into per-slot work and latent starts with a scan in LDS, then its
-// waves look their work items up by binary search, so the launch needs no
-// host-side knowledge of the row counts (and can be captured in a graph).  A
-// work item is a tile of consecutive compressed rows of one slot; a wave
-// issues the loads of all its rows before it finishes the first.
+// Prefill batches are ragged: the int32 [2, S] extend offsets become per-slot
+// work counts and latent starts on the device -- up to 64 slots in one
+// wave's lanes (a work item finds its slot with a ballot), more with a scan
+// in LDS and a binary search -- so the launch needs no host-side knowledge
+// of the row counts (and can be captured in a graph).  A work item is a tile
+// of consecutive compressed rows of one slot; a wave issues the loads of all
+// its rows before it finishes the first.
 //
 // Decode and verify batches give one wave per slot, which takes the slot's
-// tokens in order.  The ratio-2 pending tokens live in a per-slot ring (pair
+// tokens in order, or, when the ring has more entries than a call's pairs,
+// one wave per row.  The ratio-2 pending tokens live in a per-slot ring (pair
 // k in entry k % ring_slots), and under decode context parallelism the rows
 // another rank owns are computed but not stored (flashinfer_sparse.py, DCP
 // helpers).
@@ -506,7 +509,10 @@ __global__ __launch_bounds__(kBlock) void compress_prefill_kernel(CompressParams
 // decode) in order, as D single decode tokens.  Rows first: a ratio-2 token
 // at an odd position pools with the previous draft token, or for the first
 // token with the ring entry an earlier call left; the ring entries are
-// written after every row of the slot has read its inputs.
+// written after every row of the slot has read its inputs.  SPLIT (ratio 1,
+// or ring_slots > D / 2): the pairs of one call then span fewer ring entries
+// than the ring has, so no ring write can reach the entry the first row
+// reads, and each row takes a wave of its own.
 template <int L, int RATIO, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void compress_tokens_kernel(CompressParams p) {
   const PagedKV<L> kv{p.cache.base, p.cache.page_stride, p.cache.num_pages, p.cache.page_bits};
