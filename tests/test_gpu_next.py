@@ -71,10 +71,12 @@ def test_verify_batch(K, layout, ratio, explicit):
     check_compress(r, layout, 16, slots, lat)
 
 
-@pytest.mark.parametrize("D,R", [(1, 1), (2, 2), (7, 4), (16, 1)])
+@pytest.mark.parametrize("D,R", [(1, 1), (1, 3), (2, 2), (7, 4), (16, 1)])
 def test_verify_draft_lengths_and_rings(K, D, R):
     """other draft lengths, a ring too small for rollback (still exact for
-    one call: the last token sharing an entry wins) and plain decode."""
+    one call: the last token sharing an entry wins) and plain decode, with
+    one ring entry and with three (whose pending entry depends on the
+    position)."""
     _say("verify D R", D, R)
     case = W.verify_case(210 + D, 40, draft_len=D, ratio=2, page_size=8, max_pos=300,
                          ring_slots=R)
