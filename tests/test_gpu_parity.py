@@ -122,17 +122,26 @@ def test_store_rows_status_and_stride(K):
 
 
 # ===================================================================== gather
-def test_gather_c4_full(K):
-    """V41 cache of 1,048,576 rows (16384 pages x 64, random page table),
-    262,144 distinct ids -> bf16 [262144, 512]: bit-exact, every row."""
-    _say("gather C4 full")
-    c = W.workload_c4()
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gather_c4_full(K, layout):
+    """cache of 1,048,576 rows (16384 pages x 64, random page table),
+    262,144 distinct ids -> bf16 [262144, 512]: bit-exact, every row.  V41
+    is the bench's C4; V4 and V41_FP4 are the same shape in their layouts."""
+    _say("gather C4 full", layout)
+    if layout == "V41":
+        c = W.workload_c4()
+    else:
+        db, sb, rb, _ = oracle.layout_bytes(layout)
+        c = W.gather_case(W.BASE_SEED + 4, 16384, 64, 262144, rb, db, sb,
+                          scale_lo=None if layout == "V41_FP4" else 114, scale_hi=140)
     ids = c["ids"]
-    want, st = oracle.dequant_gather(c["cache"], "V41", 64, c["page_table"], ids)
+    want, st = oracle.dequant_gather(c["cache"], layout, 64, c["page_table"], ids)
     out = torch.empty((ids.size, 512), dtype=torch.int16, device="cuda")
     s = _status()
-    K.kvc_dequant_gather(K.Cache(dev(c["cache"]), "V41", 64), dev(c["page_table"]), dev(ids), out, s)
+    dc = dev(c["cache"])
+    K.kvc_dequant_gather(K.Cache(dc, layout, 64), dev(c["page_table"]), dev(ids), out, s)
     got = host(out, np.uint16)
+    del dc
     assert st == 0 and int(s.item()) == 0
     assert sha(got) == sha(want)
 
@@ -281,15 +290,17 @@ def test_compress_c1(K):
     assert np.array_equal(host(out, np.uint16), want)
 
 
-def test_compress_c3_full(K):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_compress_c3_full(K, layout):
     """16 requests totalling 32768 tokens, fused |kv|score| [32768, 1024],
-    page 128, V41_FP4, in the bench's launch configuration."""
-    _say("compress C3 full")
+    page 128, in the bench's launch configuration (the bench stores
+    V41_FP4; V41 and V4 run the same batch in their layouts)."""
+    _say("compress C3 full", layout)
     case = W.workload_c3()
-    r = _run_compress(K, case, "V41_FP4", 2, oracle.PREFILL)
+    r = _run_compress(K, case, layout, 2, oracle.PREFILL)
     lat, slots = _prefill_slots(case, 2)
     assert r["n_rows"] == int((case["lengths"] // 2).sum()) == len(lat)
-    _check_compress(r, "V41_FP4", 128, slots, lat)
+    _check_compress(r, layout, 128, slots, lat)
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
