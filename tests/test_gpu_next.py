@@ -71,6 +71,19 @@ def test_verify_batch(K, layout, ratio, explicit):
     check_compress(r, layout, 16, slots, lat)
 
 
+def test_verify_bench_size(K):
+    """the bench's verify batch: 1024 slots x 4 drafts, ring of 3, V41_FP4
+    through page tables of 64-row pages (one wave per row)."""
+    _say("verify bench size")
+    case = W.verify_case(20261206, 1024, draft_len=4, ratio=2, page_size=64, max_pos=4096,
+                         ring_slots=3)
+    r = run_compress(K, case, "V41_FP4", 2, oracle.VERIFY, page_table=case["page_table"],
+                     draft_len=4, ring_slots=3)
+    lat, slots = _token_rows(case, 2)
+    assert r["n_rows"] == len(lat)
+    check_compress(r, "V41_FP4", 64, slots, lat)
+
+
 @pytest.mark.parametrize("D,R", [(1, 1), (1, 3), (2, 2), (7, 4), (16, 1)])
 def test_verify_draft_lengths_and_rings(K, D, R):
     """other draft lengths, a ring too small for rollback (still exact for
@@ -207,6 +220,21 @@ def test_dcp_filter_ids(K, world, interleave, k):
     total = 0
     for rank in range(world):
         (ws, wl, wst), (gs, gl, gst) = _filter(K, c, world, rank, interleave)
+        assert np.array_equal(gl, wl) and np.array_equal(gs, ws) and gst == wst
+        total += int(gl.sum())
+    assert total == int(((c["ids"] >= 0) & (c["valid"][:, None] != 0)).sum())
+
+
+def test_dcp_filter_bench_size(K):
+    """the bench's filter: 4096 token rows x 2048 global ids, 32 requests,
+    4 ranks in runs of 4, every rank (bit-exact; the ranks' counts
+    partition the valid ids)."""
+    _say("dcp filter bench size")
+    c = W.dcp_ids_case(20261208, T=4096, k=2048, n_req=32, max_rows=65536, world=4,
+                       page_size=64)
+    total = 0
+    for rank in range(4):
+        (ws, wl, wst), (gs, gl, gst) = _filter(K, c, 4, rank, 4)
         assert np.array_equal(gl, wl) and np.array_equal(gs, ws) and gst == wst
         total += int(gl.sum())
     assert total == int(((c["ids"] >= 0) & (c["valid"][:, None] != 0)).sum())
