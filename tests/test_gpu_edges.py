@@ -1,7 +1,7 @@
 """Edge cases of the HIP path against the oracle, through the C ABI: the
 largest prefill batch, the smallest and largest pages, strided buffers,
-ragged gather counts, the longest draft and decode context parallelism at a
-wide group.  Same bar as the other parity tests (bytes bit-exact; fused
+ragged gather counts, the longest draft, decode context parallelism at a
+wide group and the widest DCP id rows.  Same bar as the other parity tests (bytes bit-exact; fused
 outputs within the stated tolerance)."""
 import numpy as np
 import pytest
@@ -186,3 +186,29 @@ def test_dcp_decode_wide_group(K):
                 slots.append(int(case["page_table"][b, u // 64]) * 64 + u % 64 if ow == rank else 0)
                 lat.append(b)
         check_compress(r, "V41_FP4", 64, slots, lat)
+
+
+def test_dcp_filter_widest_row(K):
+    """rows of 65,536 ids (the largest k: 32 passes of 2048), 3 ranks in
+    runs of 2 and a power-of-two group of 2 in runs of 8: slots and counts
+    equal the oracle's on every rank."""
+    c = W.dcp_ids_case(460, T=6, k=65536, n_req=3, max_rows=140000, world=3, page_size=64)
+    c2 = W.dcp_ids_case(461, T=6, k=65536, n_req=3, max_rows=140000, world=2, page_size=64)
+    for case, world, inter in ((c, 3, 2), (c2, 2, 8)):
+        ids = case["ids"]
+        for rank in range(world):
+            _say("dcp filter widest row", world, inter, rank)
+            bt = case["block_tables"][rank]
+            want = oracle.dcp_filter_ids(ids, case["token_to_req"], bt, page_size=64,
+                                         num_pages=case["num_pages"], world=world, rank=rank,
+                                         interleave=inter, valid=case["valid"])
+            T, k = ids.shape
+            out = torch.full((T, k), 12345, dtype=torch.int32, device="cuda")
+            lens = torch.full((T,), -7, dtype=torch.int32, device="cuda")
+            s = torch.zeros(1, dtype=torch.int32, device="cuda")
+            K.kvc_dcp_filter_ids(dev(ids), dev(case["token_to_req"]), dev(bt), out, lens,
+                                 page_size=64, num_pages=case["num_pages"], world=world,
+                                 rank=rank, interleave=inter, valid=dev(case["valid"]), status=s)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(lens), want[1]) and np.array_equal(host(out), want[0])
+            assert int(s.item()) == want[2]
