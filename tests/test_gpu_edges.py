@@ -1,8 +1,8 @@
 """Edge cases of the HIP path against the oracle, through the C ABI: the
 largest prefill batch, the smallest and largest pages, strided buffers,
 ragged gather counts, the longest draft, decode context parallelism at a
-wide group and the widest DCP id rows.  Same bar as the other parity tests (bytes bit-exact; fused
-outputs within the stated tolerance)."""
+wide group and the widest DCP id rows.  Same bar as the other parity tests
+(bytes bit-exact; fused outputs within the stated tolerance)."""
 import numpy as np
 import pytest
 import torch
