@@ -153,16 +153,22 @@ def test_verify_rejection_steps(K):
 
 
 # ================================================================= DCP
-@pytest.mark.parametrize("layout", ["V41", "V41_FP4"])
-def test_dcp_prefill_owner_predicate(K, layout):
+@pytest.mark.parametrize("layout,slots", [("V41", 5), ("V41_FP4", 5), ("V41_FP4", 90)])
+def test_dcp_prefill_owner_predicate(K, layout, slots):
     """prefill rows dealt over 3 ranks in runs of 2; each rank's call stores
-    its own rows at its own page-table slots."""
+    its own rows at its own page-table slots.  5 slots (lookup by ballot) and
+    90 (the LDS tables and binary search of batches over 64 slots)."""
     world, K_, ps = 3, 2, 8
-    lengths, P = [37, 0, 120, 9, 64], [0, 0, 5, 2, 31]
+    if slots == 5:
+        lengths, P = [37, 0, 120, 9, 64], [0, 0, 5, 2, 31]
+    else:
+        rng = np.random.default_rng(229)
+        lengths = [int(x) for x in rng.integers(0, 70, size=slots)]
+        P = [int(x) for x in rng.integers(0, 40, size=slots)]
     case = W.compress_case(230, lengths, start_pos=P, ratio=2, page_size=ps, fused=True, gap=2)
     tables, npg = W.per_rank_page_tables(231, world, len(lengths), case["page_table"].shape[1])
     for rank in range(world):
-        _say("dcp prefill", layout, rank)
+        _say("dcp prefill", layout, slots, rank)
         c = dict(case, page_table=tables[rank], num_pages=npg)
         r = run_compress(K, c, layout, 2, oracle.PREFILL, page_table=tables[rank],
                          dcp_world=world, dcp_rank=rank, dcp_interleave=K_)
