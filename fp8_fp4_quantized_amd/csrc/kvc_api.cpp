@@ -237,8 +237,9 @@ int kvc_dequant_gather(const kvc_cache* cache, const int32_t* page_table, int64_
   if (n == 0) return ok();
   if (ids == nullptr || out_bf16 == nullptr) return fail(KVC_EINVAL, "%s: NULL ids or output", who);
   if (page_table != nullptr && n_pages < 1) return fail(KVC_EINVAL, "%s: page table with n_pages < 1", who);
-  if (!aligned16(out_bf16) || !row_stride_ok(out_row_stride))
-    return fail(KVC_EINVAL, "%s: output must be 16-byte aligned with out_row_stride >= 512, a multiple of 8", who);
+  if (!aligned16(out_bf16) || !row_stride_ok(out_row_stride) || out_row_stride > (1 << 25))
+    return fail(KVC_EINVAL, "%s: output must be 16-byte aligned with out_row_stride in [512, 2^25], "
+                            "a multiple of 8", who);
   p.page_table = page_table;
   p.n_pages = page_table ? n_pages : 0;
   p.ids = ids;

@@ -31,6 +31,21 @@ __device__ __forceinline__ void st_u4_nt(void* p, uint4 v) {
   __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4*)p);
 }
 
+// A 16-byte streaming store at device scope: non-temporal with the sc1
+// cache-policy bit, a policy only the buffer instructions take from the
+// compiler.  For rows written once and not read back by the kernel; on the
+// gather's 268 MB of output it measured 3-4% faster than non-temporal
+// alone.  `base` must be the same on every lane (it becomes the buffer
+// descriptor: raw, stride 0, 2^31 - 1 bytes, 32-bit data format), and
+// byte_off below 2^31.
+constexpr int kCpolNtSc1 = 2 | 16;          // nt | sc1
+__device__ __forceinline__ void st_u4_stream(void* base, uint32_t byte_off, uint4 v) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, (int)byte_off, 0,
+                                         kCpolNtSc1);
+}
+
 // Gather the scale byte held by lane `stride * g` (g = 0 .. 4*W-1) into W
 // dwords, byte g of the result in byte g % 4 of dword g / 4.  Uses
 // v_readlane, so the result is wave-uniform.

@@ -324,7 +324,8 @@ __global__ __launch_bounds__(kBlock) void dequant_gather_kernel(GatherParams p) 
       for (int u = 0; u < kGatherUnroll; ++u) {
         if (j + u >= cnt) break;
         const uint4 o = s[u] >= 0 ? decode_lane<L>(c[u], lane) : make_uint4(0u, 0u, 0u, 0u);
-        st_u4_nt(p.out + (b0 + j + u) * p.out_stride + kDimsPerLane * lane, o);
+        st_u4_stream(p.out + b0 * p.out_stride,
+                     (uint32_t)(((j + u) * p.out_stride + kDimsPerLane * lane) * 2), o);
       }
     }
   }

@@ -279,7 +279,7 @@ int kvc_compress_store(const kvc_compress_args* args, void* stream);
  *               table or cache, or a page outside the cache, gives a zero row
  *               and a status bit
  *   out_bf16    device, row j at out_bf16 + j*out_row_stride elements;
- *               out_row_stride >= 512, multiple of 8; 16-B aligned
+ *               out_row_stride in [512, 2^25], multiple of 8; 16-B aligned
  * Values: fp8 code times 2^(E - 127) (V41, V4 nope dims), e2m1 code times
  * the e4m3 scale (V41_FP4), V4 rope dims copied; each product is exact in
  * bf16.  A NaN code, a ue8m0 byte of 255 or a NaN e4m3 scale gives NaN. */

@@ -95,6 +95,8 @@ def test_store_and_gather_argument_checks(kvc):
     assert L.kvc_dequant_gather(C.byref(c), FAKE, 0, FAKE, 5, FAKE, 512, None, None) == kvc.KVC_EINVAL
     assert L.kvc_dequant_gather(C.byref(c), None, 0, FAKE, 5, FAKE, 500, None, None) == kvc.KVC_EINVAL
     assert L.kvc_dequant_gather(C.byref(c), None, 0, FAKE, 5, FAKE + 8, 512, None, None) == kvc.KVC_EINVAL
+    assert L.kvc_dequant_gather(C.byref(c), None, 0, FAKE, 5, FAKE, (1 << 25) + 8, None,
+                                None) == kvc.KVC_EINVAL
     # the rotary store: same checks plus positions and the table
     rope = L.kvc_store_rows_rope
     assert rope(C.byref(c), FAKE, 512, FAKE, FAKE, 16, FAKE, 0, None, None) == kvc.KVC_OK
