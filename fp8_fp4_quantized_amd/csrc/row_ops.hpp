@@ -39,11 +39,33 @@ __device__ __forceinline__ void st_u4_nt(void* p, uint4 v) {
 // descriptor: raw, stride 0, 2^31 - 1 bytes, 32-bit data format), and
 // byte_off below 2^31.
 constexpr int kCpolNtSc1 = 2 | 16;          // nt | sc1
+constexpr int kCpolSc1 = 16;                // sc1: device scope
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF,
+                                           0x00020000);
+}
 __device__ __forceinline__ void st_u4_stream(void* base, uint32_t byte_off, uint4 v) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7FFFFFFF, 0x00020000);
-  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, (int)byte_off, 0,
-                                         kCpolNtSc1);
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, raw_rsrc(base),
+                                         (int)byte_off, 0, kCpolNtSc1);
+}
+
+// Loads at device scope (sc1) through a buffer descriptor made from a base
+// that is the same on every lane, at a 32-bit byte offset below 2^31: for
+// rows read once by one wave, with no reuse inside the compute unit.  On the
+// gather's rows they measured about 0.7% faster than plain global loads.
+__device__ __forceinline__ uint4 ld_u4_dev(const void* base, uint32_t byte_off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(raw_rsrc(base), (int)byte_off, 0, kCpolSc1);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_u2_dev(const void* base, uint32_t byte_off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(raw_rsrc(base), (int)byte_off, 0, kCpolSc1);
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ld_u32_dev(const void* base, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(raw_rsrc(base), (int)byte_off, 0, kCpolSc1);
+}
+__device__ __forceinline__ uint32_t ld_u8_dev(const void* base, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(raw_rsrc(base), (int)byte_off, 0, kCpolSc1);
 }
 
 // Gather the scale byte held by lane `stride * g` (g = 0 .. 4*W-1) into W

@@ -215,24 +215,23 @@ template <> struct LaneCodes<kV4> { uint4 raw; uint32_t scale; };
 template <int L>
 __device__ __forceinline__ LaneCodes<L> load_lane(const PagedKV<L>& kv, int64_t slot, int lane);
 
-// Plain (cached) loads: a gathered row's scale part shares its cache line
-// with the scale parts of the page's other rows, which later ids of the
-// batch often select.  (Non-temporal loads measured slower.)
+// Device-scope loads from the row's own base (the slot is the same on every
+// lane).  A gathered row's scale part shares its cache line with the scale
+// parts of the page's other rows; non-temporal loads measured slower.
 template <>
 __device__ __forceinline__ LaneCodes<kV41> load_lane<kV41>(const PagedKV<kV41>& kv, int64_t slot,
                                                            int lane) {
   LaneCodes<kV41> r;
-  const u32x2 c = *(const u32x2*)(kv.data(slot) + 8 * lane);
-  r.codes = make_uint2(c.x, c.y);
-  r.scale = kv.scale(slot)[lane >> 2];
+  r.codes = ld_u2_dev(kv.data(slot), 8u * lane);
+  r.scale = ld_u8_dev(kv.scale(slot), (uint32_t)lane >> 2);
   return r;
 }
 template <>
 __device__ __forceinline__ LaneCodes<kV41Fp4> load_lane<kV41Fp4>(const PagedKV<kV41Fp4>& kv,
                                                                  int64_t slot, int lane) {
   LaneCodes<kV41Fp4> r;
-  r.codes = *(const uint32_t*)(kv.data(slot) + 4 * lane);
-  r.scale = kv.scale(slot)[lane >> 1];
+  r.codes = ld_u32_dev(kv.data(slot), 4u * lane);
+  r.scale = ld_u8_dev(kv.scale(slot), (uint32_t)lane >> 1);
   return r;
 }
 template <>
@@ -241,11 +240,11 @@ __device__ __forceinline__ LaneCodes<kV4> load_lane<kV4>(const PagedKV<kV4>& kv,
   LaneCodes<kV4> r;
   const uint8_t* d = kv.data(slot);
   if (lane < kRopeLane0) {
-    const u32x2 c = *(const u32x2*)(d + 8 * lane);
+    const uint2 c = ld_u2_dev(d, 8u * lane);
     r.raw = make_uint4(c.x, c.y, 0u, 0u);
-    r.scale = kv.scale(slot)[lane >> 3];
+    r.scale = ld_u8_dev(kv.scale(slot), (uint32_t)lane >> 3);
   } else {
-    r.raw = ld_u4(d + kNope + 16 * (lane - kRopeLane0));
+    r.raw = ld_u4_dev(d, kNope + 16u * (lane - kRopeLane0));
     r.scale = 0;
   }
   return r;
