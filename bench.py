@@ -342,23 +342,43 @@ def main() -> int:
     elapsed = time.perf_counter() - t_start
     ms_step = elapsed * 1e3 / args.steps
 
-    # per-kernel durations: HIP events on the launch stream around runs of
-    # back-to-back launches of one kernel (an event between every two kernels
-    # would add its own gap to each interval)
+    # per-kernel durations: HIP events on the launch stream around replays of
+    # HIP graphs of 10 back-to-back launches of one kernel (the gathers with
+    # the id lists and outputs in turn).  An untimed compress replay comes
+    # first, so the device is busy when the first event is reached and no
+    # host launch latency falls inside an interval; the gathers follow the
+    # compresses, as in a step.
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        return g
+
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        compress()
+        gather(0)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g_comp = capture(lambda: [compress() for _ in range(10)])
+    g_gath = capture(lambda: [gather(k) for k in range(10)])
+    torch.cuda.synchronize()
     runs = max(args.steps // 10, 2)
     comp_ms, gath_ms = [], []
     for r in range(runs):
         a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        g_comp.replay()
         a.record(stream)
-        for _ in range(10):
-            compress()
+        g_comp.replay()
         b.record(stream)
-        for k in range(10):
-            gather(k)
+        g_gath.replay()
         c.record(stream)
         torch.cuda.synchronize()
         comp_ms.append(a.elapsed_time(b) / 10)
         gath_ms.append(b.elapsed_time(c) / 10)
+    assert int(status.item()) == 0, f"device status {int(status.item())}"
 
     comp_bytes = c3_rows * (4096 + 1024 + fp4.row_bytes) + c3_tails * 2 * 2048
     gath_bytes = n_ids * (v41.row_bytes + 1024 + 4)
