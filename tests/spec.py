@@ -81,9 +81,11 @@ def all_bf16() -> np.ndarray:
 def closed_form_ue8m0(amax_f32: np.ndarray) -> np.ndarray:
     """The exponent formula the pages print for the fp8 row quantizer:
     max((bits >> 23) - 8 + (mantissa > 0x600000), 114), bits of fp32 amax."""
-    bits = np.asarray(amax_f32, np.float32).view(np.uint32).astype(np.int64)
-    e = (bits >> 23) - 8 + ((bits & 0x7FFFFF) > 0x600000)
-    return np.maximum(e, 114)
+    bits = np.asarray(amax_f32, np.float32).view(np.uint32)
+    e = (bits >> 23).view(np.int32)              # exponent field, below 2^9
+    e -= 8
+    e += (bits & 0x7FFFFF) > 0x600000
+    return np.maximum(e, 114, out=e)
 
 
 # ---------------------------------------------------------------- compressor

@@ -70,6 +70,19 @@ def test_ue8m0_closed_form_fp32_samples_and_boundaries():
     assert np.all(oracle.ue8m0(den) == 114)
 
 
+def test_ue8m0_closed_form_every_positive_fp32():
+    """The closed form against the oracle's definition (the smallest k >= -13
+    with 448 * 2^k >= amax) on every positive finite fp32 amax, 2^31 - 2^23
+    values in chunks (small enough to reuse warm memory)."""
+    step = 1 << 20
+    for lo in range(0, 0x7F800000, step):
+        amax = np.arange(lo, min(lo + step, 0x7F800000), dtype=np.uint32).view(np.float32)
+        got = oracle.ue8m0(amax)
+        ref = spec.closed_form_ue8m0(amax)
+        bad = np.flatnonzero(got != ref)
+        assert bad.size == 0, (hex(lo + int(bad[0])), int(got[bad[0]]), int(ref[bad[0]]))
+
+
 def test_ue8m0_against_log2_formula():
     """Against ceil(log2(max(amax/448, 1e-4))) evaluated by math.log2 on
     values away from exact powers of two, and hand-worked values."""
