@@ -145,6 +145,20 @@ def measure_next_rows(kvc, W, d, dev, stream):
     rrows, rloc = d(c2["rows"]), d(c2["out_loc"])
     secs = _time_events(lambda: kvc.kvc_store_rows(rcache, rrows, rloc, status), stream, 50)
     entry("store_c2_v41fp4", secs, n2 * (1024 + fp4.row_bytes + 4), n2, "rows_per_s")
+    # the dequant half of the same workload: every stored row back to bf16 by
+    # its slot (no page table)
+    dq_out = torch.empty((n2, 512), dtype=torch.int16, device=dev)
+    secs = _time_events(lambda: kvc.kvc_dequant_gather(rcache, None, rloc, dq_out, status),
+                        stream, 50)
+    entry("dequant_c2_v41fp4", secs, n2 * (fp4.row_bytes + 1024 + 4), n2, "rows_per_s")
+    v41c = kvc.kvc_layout_query("V41")
+    vcache = kvc.Cache(torch.zeros((c2["num_pages"], 64 * v41c.row_bytes), dtype=torch.uint8,
+                                   device=dev), "V41", 64)
+    secs = _time_events(lambda: kvc.kvc_store_rows(vcache, rrows, rloc, status), stream, 50)
+    entry("store_c2_v41", secs, n2 * (1024 + v41c.row_bytes + 4), n2, "rows_per_s")
+    secs = _time_events(lambda: kvc.kvc_dequant_gather(vcache, None, rloc, dq_out, status),
+                        stream, 50)
+    entry("dequant_c2_v41", secs, n2 * (v41c.row_bytes + 1024 + 4), n2, "rows_per_s")
     secs = _time_events(lambda: kvc.kvc_store_rows_rope(rcache, rrows, pos2, fr2, rloc, status),
                         stream, 50)
     entry("rope_store_c2_v41fp4", secs, n2 * (1024 + fp4.row_bytes + 8), n2, "rows_per_s")
@@ -202,6 +216,7 @@ def measure_next_rows(kvc, W, d, dev, stream):
     res["graph_c1_compress"] = {"eager_us_per_call": eager * 1e6,
                                 "graph_us_per_call": replay * 1e6,
                                 "calls_per_graph": 20, "calls": n_calls}
+    assert int(status.item()) == 0, f"device status {int(status.item())}"
     return res
 
 

@@ -79,13 +79,4 @@ __device__ __forceinline__ float div_by_rcp(float x, float s, float rs) {
   return __builtin_copysignf(__builtin_fmaf(r, rs, q0), x);
 }
 
-// exact fp32 value of an e4m3fn code (NaN codes excluded by the caller)
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  const float sub = (float)m * 0x1p-9f;
-  const float mag = e == 0 ? sub : nrm;
-  return (c & 0x80u) ? -mag : mag;
-}
-
 }  // namespace kvc

@@ -270,23 +270,22 @@ __device__ __forceinline__ uint4 dq_fp8x8(uint2 codes, uint32_t E) {
 }
 
 // 8 e2m1 codes (nibbles, dim order from the low nibble) + their e4m3 scale
-// code -> 8 bf16.  The e2m1 magnitude's low 3 bits placed at bit 22 of an
-// fp32 give the value times 2^-126; the product with the scale is exact
-// (at most 7 significant bits, far from the fp32 and bf16 limits).
-__device__ __forceinline__ uint32_t dq_fp4_one(uint32_t n, float s) {
-  const float f = __uint_as_float(((n & 0x8u) << 28) | ((n & 0x7u) << 22));
-  return bf16_top(__builtin_amdgcn_ldexpf(f * s, 126));
-}
+// code -> 8 bf16.  The hardware converts the scale code and a byte's two
+// codes to fp32 (the codes at unit scale); the product is exact in fp32 (at
+// most 7 significant bits, far from the fp32 and bf16 limits), so its top
+// half is the bf16.  A NaN scale code makes every product a quiet NaN, whose
+// top half is a bf16 NaN.
 __device__ __forceinline__ uint4 dq_fp4x8(uint32_t w, uint32_t sc) {
-  if ((sc & 0x7Fu) == 0x7Fu) return make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-  const float s = e4m3_to_f32(sc);
-  uint32_t o[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t b = w >> (8 * k);
-    o[k] = dq_fp4_one(b & 0xFu, s) | (dq_fp4_one((b >> 4) & 0xFu, s) << 16);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
+  auto pair = [&](f32x2 f) -> uint32_t {
+    // bytes 2, 3 of the first product, then bytes 2, 3 of the second
+    return __builtin_amdgcn_perm(__float_as_uint(f[1] * s), __float_as_uint(f[0] * s),
+                                 0x07060302u);
+  };
+  return make_uint4(pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)),
+                    pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)),
+                    pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)),
+                    pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3)));
 }
 
 }  // namespace kvc

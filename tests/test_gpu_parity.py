@@ -92,7 +92,8 @@ def test_fp4_dequant_all_codes_all_scales(K):
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_store_rows_c2(K, layout):
     """Ratio-1 store of 8 requests (extend lengths in [512, 4096], outlier
-    rows, 1% zero rows), page 64: bit-exact cache image."""
+    rows, 1% zero rows), page 64: bit-exact cache image; then the dequant of
+    every stored row by its physical slot (no page table): bit-exact bf16."""
     _say("store C2", layout)
     c = W.workload_c2()
     rows, out_loc = c["rows"], c["out_loc"].copy()
@@ -100,10 +101,18 @@ def test_store_rows_c2(K, layout):
     hc, dc = _cache_pair(c["num_pages"], 64, layout)
     st = oracle.store_rows(hc, layout, 64, rows, out_loc)
     s = _status()
-    K.kvc_store_rows(K.Cache(dc, layout, 64), dev(rows), dev(out_loc), s)
+    cache = K.Cache(dc, layout, 64)
+    K.kvc_store_rows(cache, dev(rows), dev(out_loc), s)
     got = host(dc)
     assert st == 0 and int(s.item()) == 0
     assert sha(got) == sha(hc), np.argwhere(got != hc)[:5]
+    # dequant by slot; the padded row's id is -1 (a zero row)
+    ids = np.where(out_loc == 0, -1, out_loc).astype(np.int32)
+    want, gst = oracle.dequant_gather(hc, layout, 64, None, ids)
+    out = torch.empty((ids.size, 512), dtype=torch.int16, device="cuda")
+    K.kvc_dequant_gather(cache, None, dev(ids), out, s)
+    assert gst == 0 and int(s.item()) == 0
+    assert sha(host(out).view(np.uint16)) == sha(want)
 
 
 def test_store_rows_status_and_stride(K):
