@@ -78,6 +78,7 @@ struct GatherParams {
   uint16_t* out;
   int64_t out_stride;          // elements
   int32_t* status;
+  int32_t batch;               // ids a wave resolves at once: 8, 16 or 32 (set by the launcher)
 };
 
 struct CompressParams {

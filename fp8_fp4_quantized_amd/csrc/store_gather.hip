@@ -202,10 +202,11 @@ __global__ __launch_bounds__(kBlock) void dcp_filter_kernel(DcpFilterParams p) {
 }
 
 // ------------------------------------------------------------------ gather
-// rows handled together by one wave per loop trip, and ids one wave
-// resolves per batch
+// rows handled together by one wave per loop trip, and the most ids one
+// wave resolves per batch
 constexpr int kGatherUnroll = 8;
 constexpr int kGatherBatch = 32;
+constexpr int kGatherMinBatch = 8;
 
 template <int L> struct LaneCodes;          // this lane's share of a row
 template <> struct LaneCodes<kV41> { uint2 codes; uint32_t scale; };
@@ -266,12 +267,13 @@ __device__ __forceinline__ uint4 decode_lane<kV4>(const LaneCodes<kV4>& c, int l
   return dq_fp8x8(make_uint2(c.raw.x, c.raw.y), c.scale);
 }
 
-// A wave takes the rows of the gather kGatherBatch at a time: lane i reads
-// id i of the batch and resolves it to a physical slot (one vector load of
-// ids, one of page-table entries), then the rows are expanded kGatherUnroll
-// at a time, their slots broadcast with v_readlane, all their loads issued
-// before any store.  32-id batches give 8192 waves for 262,144 ids, about
-// one resident round of the chip (measured faster than 16, 48 or 64).
+// A wave takes the rows of the gather p.batch at a time: lane i reads id i
+// of the batch and resolves it to a physical slot (one vector load of ids,
+// one of page-table entries), then the rows are expanded kGatherUnroll at a
+// time, their slots broadcast with v_readlane, all their loads issued before
+// any store.  32-id batches give 8192 waves for 262,144 ids, about one
+// resident round of the chip (measured faster than 16, 48 or 64); a smaller
+// gather takes smaller batches, so that its rows spread over more waves.
 template <int L>
 __global__ __launch_bounds__(kBlock) void dequant_gather_kernel(GatherParams p) {
   const PagedKV<L> kv = paged<L>(p.cache);
@@ -280,12 +282,13 @@ __global__ __launch_bounds__(kBlock) void dequant_gather_kernel(GatherParams p) 
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const int32_t page_mask = (1 << p.cache.page_bits) - 1;
 
-  for (int64_t b0 = wave0 * kGatherBatch; b0 < p.n; b0 += nwaves * kGatherBatch) {
+  const int32_t batch = p.batch;
+  for (int64_t b0 = wave0 * batch; b0 < p.n; b0 += nwaves * batch) {
     // ---- resolve this lane's id to a slot (-1: zero row)
     const int64_t r = b0 + lane;
     int32_t slot = -1;
     int32_t bad = 0;
-    if (lane < kGatherBatch && r < p.n) {
+    if (lane < batch && r < p.n) {
       const int32_t id = p.ids[r];
       if (id >= 0) {
         if (p.page_table != nullptr) {
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(kBlock) void dequant_gather_kernel(GatherParams p) 
     if (bad != 0 && p.status != nullptr) atomicOr(p.status, bad);
 
     // ---- expand the batch's rows
-    const int cnt = (int)(p.n - b0 < kGatherBatch ? p.n - b0 : kGatherBatch);
+    const int cnt = (int)(p.n - b0 < batch ? p.n - b0 : batch);
     for (int j = 0; j < cnt; j += kGatherUnroll) {
       int32_t s[kGatherUnroll];
       LaneCodes<L> c[kGatherUnroll];
@@ -372,8 +375,13 @@ hipError_t launch_dcp_filter(const DcpFilterParams& p, hipStream_t stream) {
                            : launch(dcp_filter_kernel<false>, blocks, p, stream);
 }
 
-hipError_t launch_dequant_gather(const GatherParams& p, hipStream_t stream) {
-  int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * kGatherBatch, 8192);
+hipError_t launch_dequant_gather(const GatherParams& p_in, hipStream_t stream) {
+  // batches of 32 from 2^17 ids up, smaller below: at least 4096 waves
+  // where the ids allow, one per 8 ids at the fewest
+  GatherParams p = p_in;
+  p.batch = kGatherBatch;
+  while (p.batch > kGatherMinBatch && p.n < (int64_t)p.batch * 4096) p.batch >>= 1;
+  int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * p.batch, 8192);
   if (launch_tuning().gather_blocks > 0) blocks = launch_tuning().gather_blocks;
   switch (p.cache.layout) {
     case kV41: return launch(dequant_gather_kernel<kV41>, blocks, p, stream);
