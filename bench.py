@@ -259,6 +259,87 @@ def measure_reuse(kvc, cache, pt, idsets, outs, stream, layers: int, forwards: i
     return res
 
 
+def measure_sweep(kvc, W, d, dev, stream):
+    """Throughput against size: the prefill compress at 1, 2, 4 and 8 times
+    the 32,768-token workload (16 requests per 32,768 ragged tokens, fused
+    |kv|score| buffer, page 128, V41_FP4), and the gather from the 1,048,576-row
+    V41 cache at 65,536 to 1,048,576 distinct ids (four id lists and three
+    outputs in turn).  Each size is timed as graph replays of back-to-back
+    calls, like the next rows, with its inputs and outputs in turn."""
+    import numpy as np
+    import torch
+
+    fp4 = kvc.kvc_layout_query("V41_FP4")
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    out = []
+    for mult in (1, 2, 4, 8):
+        rng = np.random.default_rng(W.BASE_SEED + 100 + mult)
+        S = 16 * mult
+        lengths = W.ragged_lengths(rng, 32768 * mult, S)
+        first = np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int32)
+        pages = (lengths // 2) // 128 + 2                # every compressed row's page, plus one
+        num_pages = int(pages.sum()) + 5
+        perm = W.random_pages(rng, int(pages.sum()), num_pages)
+        pt = np.zeros((S, int(pages.max())), np.int32)
+        k = 0
+        for b in range(S):
+            pt[b, :pages[b]] = perm[k:k + pages[b]]
+            k += pages[b]
+        T = int(lengths.sum())
+        gen.manual_seed(W.BASE_SEED + mult)
+        proj = torch.randn((T, 1024), device=dev, generator=gen).to(torch.bfloat16).view(torch.int16)
+        rows, tails = int((lengths // 2).sum()), int((lengths % 2).sum())
+        # copies of the input and of the outputs in turn, at least 512 MB of
+        # input in all: no call reads or rewrites what an earlier one left in
+        # the 256 MB Infinity Cache
+        ncopy = max(3, -(-(1 << 29) // (T * 2048)))
+        projs = [proj] + [proj.clone() for _ in range(ncopy - 1)]
+        lats = [torch.empty((rows, 512), dtype=torch.int16, device=dev) for _ in range(ncopy)]
+        caches = [kvc.Cache(torch.zeros((num_pages, 128 * fp4.row_bytes), dtype=torch.uint8,
+                                        device=dev), "V41_FP4", 128) for _ in range(ncopy)]
+        args = dict(ratio=2, mode=kvc.MODE_PREFILL, start_pos=d(np.zeros(S, np.int32)),
+                    offsets=d(np.stack([first, lengths]).astype(np.int32)), page_table=d(pt),
+                    state=torch.zeros((S, 2, 512), dtype=torch.int16, device=dev),
+                    norm_w=d(W.norm_weight(rng)), eps=1e-6,
+                    freqs=d(W.rope_freqs(int(lengths.max()) + 2)), status=status)
+        turn = [0]
+
+        def comp():
+            k = turn[0]
+            turn[0] += 1
+            pj = projs[k % ncopy]
+            kvc.kvc_compress_store(**args, kv=pj[:, :512], score=pj[:, 512:],
+                                   latent_out=lats[k % ncopy], cache=caches[k % ncopy])
+        secs = _time_events(comp, stream, 2 * ncopy)
+        nbytes = rows * (4096 + 1024 + fp4.row_bytes) + tails * 4096
+        out.append({"kernel": "compress_store", "tokens": T, "requests": S, "rows": rows,
+                    "us": secs * 1e6, "bytes": nbytes, "gbps": nbytes / secs / 1e9,
+                    "frac": nbytes / secs / 1e9 / HBM_PEAK_GBS})
+        del proj, projs, lats, caches, args
+        torch.cuda.empty_cache()
+    c4 = W.workload_c4()
+    cache, pt = kvc.Cache(d(c4["cache"]), "V41", 64), d(c4["page_table"])
+    for n in (65536, 262144, 524288, 1048576):
+        sets = [d(np.random.default_rng(W.BASE_SEED + 200 + j).choice(
+            1048576, size=n, replace=False).astype(np.int32)) for j in range(4)]
+        outs = [torch.empty((n, 512), dtype=torch.int16, device=dev) for _ in range(3)]
+        turn = [0]
+
+        def call():
+            k = turn[0]
+            turn[0] += 1
+            kvc.kvc_dequant_gather(cache, pt, sets[k % 4], outs[k % 3], status)
+        secs = _time_events(call, stream, 12)
+        nbytes = n * (528 + 1024 + 4)
+        out.append({"kernel": "dequant_gather", "ids": n, "us": secs * 1e6, "bytes": nbytes,
+                    "gbps": nbytes / secs / 1e9, "frac": nbytes / secs / 1e9 / HBM_PEAK_GBS})
+        del sets, outs
+        torch.cuda.empty_cache()
+    assert int(status.item()) == 0, f"device status {int(status.item())}"
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +351,9 @@ def main() -> int:
     ap.add_argument("--gather-blocks", type=int, default=0)
     ap.add_argument("--compress-blocks", type=int, default=0)
     ap.add_argument("--compress-tile-rows", type=int, default=0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="only measure compress and gather throughput at several sizes, one "
+                         "JSON line per size, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (the known-size "
                          "reference for the HBM byte counters) and exit")
@@ -297,6 +381,13 @@ def main() -> int:
                           "launches": 5}), flush=True)
         return 0
     kvc.kvc_set_launch_shape(args.gather_blocks, args.compress_blocks, args.compress_tile_rows)
+    if args.sweep:
+        def d(a):
+            a = np.ascontiguousarray(a)
+            return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+        for rec in measure_sweep(kvc, W, d, dev, torch.cuda.current_stream()):
+            print(json.dumps(rec), flush=True)
+        return 0
 
     def d(a):
         a = np.ascontiguousarray(a)
@@ -313,14 +404,19 @@ def main() -> int:
     fp4 = kvc.kvc_layout_query("V41_FP4")
     v41 = kvc.kvc_layout_query("V41")
 
+    # four copies of the projection buffer (64 MB each) and three latent
+    # outputs and caches used in turn, like the gather's id lists and outputs
+    # below: back-to-back compresses read and write HBM, not lines the
+    # previous call left in the 256 MB Infinity Cache
     proj = d(c3["kv"])
+    c3_projs = [proj] + [proj.clone() for _ in range(3)]
+    c3_lats = [torch.empty((c3_rows, 512), dtype=torch.int16, device=dev) for _ in range(3)]
+    c3_caches = [kvc.Cache(torch.zeros((c3["num_pages"], 128 * fp4.row_bytes), dtype=torch.uint8,
+                                       device=dev), "V41_FP4", 128) for _ in range(3)]
     c3_args = dict(
-        ratio=2, mode=kvc.MODE_PREFILL, kv=proj[:, :512], score=proj[:, 512:],
+        ratio=2, mode=kvc.MODE_PREFILL,
         start_pos=d(c3["start_pos"]), offsets=d(c3["offsets"]), page_table=d(c3["page_table"]),
-        state=d(c3["state"]), norm_w=d(c3["norm_w"]), eps=c3["eps"], freqs=d(c3["freqs"]),
-        latent_out=torch.empty((c3_rows, 512), dtype=torch.int16, device=dev),
-        cache=kvc.Cache(torch.zeros((c3["num_pages"], 128 * fp4.row_bytes), dtype=torch.uint8,
-                                    device=dev), "V41_FP4", 128))
+        state=d(c3["state"]), norm_w=d(c3["norm_w"]), eps=c3["eps"], freqs=d(c3["freqs"]))
     g_cache = kvc.Cache(d(c4["cache"]), "V41", 64)
     g_pt = d(c4["page_table"])
     n_ids = int(c4["ids"].size)
@@ -334,14 +430,16 @@ def main() -> int:
 
     stream = torch.cuda.current_stream()
 
-    def compress():
-        kvc.kvc_compress_store(**c3_args, status=status)
+    def compress(k):
+        pj = c3_projs[k % 4]
+        kvc.kvc_compress_store(**c3_args, kv=pj[:, :512], score=pj[:, 512:],
+                               latent_out=c3_lats[k % 3], cache=c3_caches[k % 3], status=status)
 
     def gather(k):
         kvc.kvc_dequant_gather(g_cache, g_pt, g_idsets[k % 4], g_outs[k % 3], status)
 
     def step(k):
-        compress()
+        compress(k)
         gather(k)
 
     # ---------------------------------------------------------------- timing
@@ -358,8 +456,8 @@ def main() -> int:
     ms_step = elapsed * 1e3 / args.steps
 
     # per-kernel durations: HIP events on the launch stream around replays of
-    # HIP graphs of 10 back-to-back launches of one kernel (the gathers with
-    # the id lists and outputs in turn).  An untimed compress replay comes
+    # HIP graphs of 10 back-to-back launches of one kernel (each with its
+    # inputs and outputs in turn).  An untimed compress replay comes
     # first, so the device is busy when the first event is reached and no
     # host launch latency falls inside an interval; the gathers follow the
     # compresses, as in a step.
@@ -373,11 +471,11 @@ def main() -> int:
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.stream(side):
-        compress()
+        compress(0)
         gather(0)
     stream.wait_stream(side)
     torch.cuda.synchronize()
-    g_comp = capture(lambda: [compress() for _ in range(10)])
+    g_comp = capture(lambda: [compress(k) for k in range(10)])
     g_gath = capture(lambda: [gather(k) for k in range(10)])
     torch.cuda.synchronize()
     runs = max(args.steps // 10, 2)

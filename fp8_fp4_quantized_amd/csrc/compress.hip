@@ -10,12 +10,12 @@
 // metadata kernels", Summary and Review; sglang PR #46230, summary.)
 //
 // Prefill batches are ragged: the int32 [2, S] extend offsets become per-slot
-// work counts and latent starts on the device -- up to 64 slots in one
-// wave's lanes (a work item finds its slot with a ballot), more with a scan
-// in LDS and a binary search -- so the launch needs no host-side knowledge
-// of the row counts (and can be captured in a graph).  A work item is a tile
-// of consecutive compressed rows of one slot; a wave issues the loads of all
-// its rows before it finishes the first.
+// work counts and latent starts on the device -- up to 256 slots in one
+// wave's lanes, one, two or four per lane (a work item finds its slot with
+// as many ballots), more with a scan in LDS and a binary search -- so the
+// launch needs no host-side knowledge of the row counts (and can be captured
+// in a graph).  A work item is a tile of consecutive compressed rows of one
+// slot; a wave issues the loads of all its rows before it finishes the first.
 //
 // Decode and verify batches give one wave per slot, which takes the slot's
 // tokens in order, or, when the ring has more entries than a call's pairs,
@@ -472,8 +472,94 @@ __global__ __launch_bounds__(kBlock) void compress_prefill_small_kernel(Compress
   }
 }
 
-// Prefill with any number of slots (up to kMaxPrefillSlots): the per-slot
-// prefix sums go to LDS and work items find their slot by binary search.
+// Prefill with 65 to 64 * SPL slots (SPL = 2 or 4): lane l holds slots
+// l * SPL .. l * SPL + SPL - 1 (their work counts and inclusive prefix sums,
+// in slot order), and a work item finds its slot with SPL ballots -- no LDS,
+// no barrier.
+template <int L, int RATIO, int kTileRows, int SPL>
+__global__ __launch_bounds__(kBlock) void compress_prefill_multi_kernel(CompressParams p) {
+  const PagedKV<L> kv{p.cache.base, p.cache.page_stride, p.cache.num_pages, p.cache.page_bits};
+  const int lane = lane_id();
+  const int S = p.num_slots;
+  int32_t first[SPL], n[SPL], P[SPL], items[SPL], rows[SPL];
+#pragma unroll
+  for (int k = 0; k < SPL; ++k) {
+    const int s = lane * SPL + k;
+    first[k] = n[k] = P[k] = 0;
+    if (s < S) {
+      first[k] = p.offsets[s];
+      n[k] = p.offsets[S + s];
+      P[k] = p.start_pos[s];
+    }
+  }
+  const uint4 wr = ld_u4(p.norm_w + kDimsPerLane * lane);
+  int32_t tot_i = 0, tot_r = 0;
+#pragma unroll
+  for (int k = 0; k < SPL; ++k) {
+    const SlotWork sw = lane * SPL + k < S ? slot_work<RATIO>(n[k], P[k], p.tile_log2)
+                                           : SlotWork{0, 0, 0, false};
+    items[k] = sw.items;
+    rows[k] = sw.rows;
+    tot_i += sw.items;
+    tot_r += sw.rows;
+  }
+  // inclusive scan of the lanes' totals, then each slot's inclusive sums
+  int32_t inc_i = tot_i, inc_r = tot_r;
+#pragma unroll
+  for (int d = 1; d < kLanes; d <<= 1) {
+    const int32_t ti = __shfl_up(inc_i, d), tr = __shfl_up(inc_r, d);
+    if (lane >= d) {
+      inc_i += ti;
+      inc_r += tr;
+    }
+  }
+  int32_t ci[SPL], cr[SPL];
+  {
+    int32_t ri = inc_i - tot_i, rr = inc_r - tot_r;
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+      ri += items[k];
+      rr += rows[k];
+      ci[k] = ri;
+      cr[k] = rr;
+    }
+  }
+  const float w[8] = {bf16_lo(wr.x), bf16_hi(wr.x), bf16_lo(wr.y), bf16_hi(wr.y),
+                      bf16_lo(wr.z), bf16_hi(wr.z), bf16_lo(wr.w), bf16_hi(wr.w)};
+  const int32_t total = __builtin_amdgcn_readlane(inc_i, kLanes - 1);
+  const int32_t wave0 = uniform((int32_t)blockIdx.x * kWavesPerBlock + (int32_t)(threadIdx.x >> 6));
+  const int32_t nwaves = (int32_t)gridDim.x * kWavesPerBlock;
+  for (int32_t item = wave0; item < total; item += nwaves) {
+    // slot b = number of slots whose items all come before this one
+    int32_t b = 0;
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) b += __builtin_popcountll(__ballot(ci[k] <= item));
+    const int32_t bl = b / SPL, bk = b % SPL;              // its lane and register
+    int32_t v_rows = rows[0], v_ci = ci[0], v_items = items[0], v_cr = cr[0];
+    int32_t v_first = first[0], v_n = n[0], v_P = P[0];
+#pragma unroll
+    for (int k = 1; k < SPL; ++k) {
+      if (bk == k) {
+        v_rows = rows[k];
+        v_ci = ci[k];
+        v_items = items[k];
+        v_cr = cr[k];
+        v_first = first[k];
+        v_n = n[k];
+        v_P = P[k];
+      }
+    }
+    const int32_t nrows = __builtin_amdgcn_readlane(v_rows, bl);
+    const int32_t kt = item - (__builtin_amdgcn_readlane(v_ci, bl) - __builtin_amdgcn_readlane(v_items, bl));
+    const int32_t lat0 = __builtin_amdgcn_readlane(v_cr, bl) - nrows;
+    run_tile<L, RATIO, kTileRows>(p, kv, w, b, kt, lat0, nrows, __builtin_amdgcn_readlane(v_first, bl),
+                                  __builtin_amdgcn_readlane(v_n, bl), __builtin_amdgcn_readlane(v_P, bl));
+  }
+}
+
+// Prefill with any number of slots (up to kMaxPrefillSlots; used above 256):
+// the per-slot prefix sums go to LDS and work items find their slot by
+// binary search.
 template <int L, int RATIO, int kTileRows>
 __global__ __launch_bounds__(kBlock) void compress_prefill_kernel(CompressParams p) {
   extern __shared__ int32_t tables[];
@@ -625,10 +711,18 @@ hipError_t launch_one(const CompressParams& p, hipStream_t stream) {
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     const size_t lds = sizeof(int32_t) * 2 * (size_t)(p.num_slots + 1);
-    const bool small = p.num_slots <= kLanes;
+    // up to 256 slots: slot lookup by ballots over 1, 2 or 4 slots per lane
+    const int spl = p.num_slots <= kLanes ? 1 : p.num_slots <= 2 * kLanes ? 2
+                  : p.num_slots <= 4 * kLanes ? 4 : 0;
 #define KVC_PREFILL_LAUNCH(R)                                                                     \
-  if (small)                                                                                      \
+  if (spl == 1)                                                                                   \
     hipLaunchKernelGGL((compress_prefill_small_kernel<L, RATIO, R>), dim3((int)blocks),           \
+                       dim3(kBlock), 0, stream, p);                                               \
+  else if (spl == 2)                                                                              \
+    hipLaunchKernelGGL((compress_prefill_multi_kernel<L, RATIO, R, 2>), dim3((int)blocks),        \
+                       dim3(kBlock), 0, stream, p);                                               \
+  else if (spl == 4)                                                                              \
+    hipLaunchKernelGGL((compress_prefill_multi_kernel<L, RATIO, R, 4>), dim3((int)blocks),        \
                        dim3(kBlock), 0, stream, p);                                               \
   else                                                                                            \
     hipLaunchKernelGGL((compress_prefill_kernel<L, RATIO, R>), dim3((int)blocks), dim3(kBlock),  \

@@ -153,11 +153,13 @@ def test_verify_rejection_steps(K):
 
 
 # ================================================================= DCP
-@pytest.mark.parametrize("layout,slots", [("V41", 5), ("V41_FP4", 5), ("V41_FP4", 90)])
+@pytest.mark.parametrize("layout,slots", [("V41", 5), ("V41_FP4", 5), ("V41_FP4", 90),
+                                          ("V41_FP4", 300)])
 def test_dcp_prefill_owner_predicate(K, layout, slots):
     """prefill rows dealt over 3 ranks in runs of 2; each rank's call stores
-    its own rows at its own page-table slots.  5 slots (lookup by ballot) and
-    90 (the LDS tables and binary search of batches over 64 slots)."""
+    its own rows at its own page-table slots.  5 and 90 slots (lookup by
+    ballots over one and two slots per lane) and 300 (the LDS tables and
+    binary search of batches over 256 slots)."""
     world, K_, ps = 3, 2, 8
     if slots == 5:
         lengths, P = [37, 0, 120, 9, 64], [0, 0, 5, 2, 31]
@@ -495,11 +497,12 @@ def test_fp4_quantizer_every_value_every_scale(K):
 
 # ================================================================= launch shapes
 @pytest.mark.parametrize("tile_rows", [1, 2, 4])
-@pytest.mark.parametrize("layout,ratio,slots", [("V41_FP4", 2, 9), ("V41", 1, 9), ("V4", 2, 90)])
+@pytest.mark.parametrize("layout,ratio,slots", [("V41_FP4", 2, 9), ("V41", 1, 9), ("V4", 2, 90),
+                                               ("V41_FP4", 2, 200), ("V41", 1, 300)])
 def test_prefill_every_tile_shape(K, tile_rows, layout, ratio, slots):
     """The prefill compressor under each work-item shape (rows per item 1, 2
-    or 4), small (<= 64 slots) and large slot counts: same rows as the
-    oracle."""
+    or 4) and each slot lookup (one, two or four slots per lane up to 256
+    slots; LDS tables above): same rows as the oracle."""
     _say("tile shape", tile_rows, layout, ratio, slots)
     rng = np.random.default_rng(300 + slots + ratio)
     lengths = rng.integers(0, 90, size=slots)

@@ -266,14 +266,16 @@ def test_compress_prefill_ragged(K, layout, ratio):
     _check_compress(r, layout, 16, slots, lat)
 
 
+@pytest.mark.parametrize("slots", [65, 150, 256, 300])
 @pytest.mark.parametrize("layout,ratio", [("V41_FP4", 2), ("V41", 1), ("V4", 2)])
-def test_compress_prefill_many_slots(K, layout, ratio):
-    """more slots than a wave has lanes (the LDS-table path): 150 slots with
-    lengths 0..40 and random (odd and even) start positions."""
-    _say("compress many slots", layout, ratio)
-    rng = np.random.default_rng(123 + ratio)
-    lengths = rng.integers(0, 41, size=150)
-    P = rng.integers(0, 200, size=150)
+def test_compress_prefill_many_slots(K, layout, ratio, slots):
+    """more slots than a wave has lanes, with lengths 0..40 and random (odd
+    and even) start positions: 65 and 150 / 256 slots (two / four slots per
+    lane, found by ballots) and 300 (LDS tables and a binary search)."""
+    _say("compress many slots", layout, ratio, slots)
+    rng = np.random.default_rng(123 + ratio + slots)
+    lengths = rng.integers(0, 41, size=slots)
+    P = rng.integers(0, 200, size=slots)
     case = W.compress_case(90 + ratio, lengths, start_pos=P, ratio=ratio, page_size=8,
                            fused=True, gap=1)
     r = _run_compress(K, case, layout, ratio, oracle.PREFILL)
