@@ -250,8 +250,6 @@ __device__ __forceinline__ uint4 rope_row_exact(uint4 x, float f) {
 }
 
 // ------------------------------------------------------------------ dequant
-__device__ __forceinline__ uint32_t bf16_top(float f) { return __float_as_uint(f) >> 16; }
-
 // 8 fp8 codes + their ue8m0 exponent E -> 8 bf16.  gfx950's scaled
 // conversion v_cvt_scalef32_pk_bf16_fp8 multiplies two e4m3fn codes by the
 // power of two whose biased exponent is the fp32 scale's exponent field -- E
