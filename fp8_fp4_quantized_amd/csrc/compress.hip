@@ -5,9 +5,9 @@
 // the two scores (ratio 2), RMS-normalises over the 512 dims (one wave sum),
 // writes the pre-RoPE latent, rotates the 64 rope dims (lanes 56..63, four
 // pairs per lane; the table entries reach them by lane shuffles), rounds to
-// bf16 and quantizes the row
-// into its paged slot.  (sglang PR #39652 "dsv4.1: compression, KV I/O, and
-// metadata kernels", Summary and Review; sglang PR #46230, summary.)
+// bf16 and quantizes the row into its paged slot.  (sglang PR #39652
+// "dsv4.1: compression, KV I/O, and metadata kernels", Summary and Review;
+// sglang PR #46230, summary.)
 //
 // Prefill batches are ragged: the int32 [2, S] extend offsets become per-slot
 // work counts and latent starts on the device -- up to 256 slots in one

@@ -1,11 +1,12 @@
-// store_gather.hip -- plain quantize-store of bf16 rows and the paged
-// dequant-gather (gfx950).
+// store_gather.hip -- plain quantize-store of bf16 rows, the DCP id filter
+// and the paged dequant-gather (gfx950).
 //
-// Both kernels put one 512-dim row on one 64-lane wave (8 dims per lane), so
-// every global access of a row is one contiguous, fully used span: the bf16
-// row (1024 B), the data part (512 / 256 / 576 B) and the scale part.  A wave
-// runs several rows per loop trip so that their loads are in flight
-// together; the grid strides over the rows.
+// The store and the gather put one 512-dim row on one 64-lane wave (8 dims
+// per lane), so every global access of a row is one contiguous, fully used
+// span: the bf16 row (1024 B), the data part (512 / 256 / 576 B) and the
+// scale part.  A wave runs several rows per loop trip so that their loads are
+// in flight together; the grid strides over the rows.  The filter puts one
+// row of global ids on one wave.
 #include "launch.hpp"
 #include "row_ops.hpp"
 
