@@ -116,6 +116,32 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+_I32_T = (torch.int32,)
+_F32_T = (torch.float32,)
+_B16_T = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _dense(t, dtypes, name: str) -> int:
+    """Pointer of a contiguous device tensor of one of ``dtypes``."""
+    if not (t.is_cuda and t.dtype in dtypes and t.is_contiguous()):
+        raise ValueError(f"{name}: expected a contiguous device tensor of {dtypes}, got "
+                         f"{t.dtype} {tuple(t.shape)} strides {t.stride()} on {t.device}")
+    return t.data_ptr()
+
+
+def _rows(t, dtypes, name: str) -> int:
+    """Pointer of a 2-D device tensor of ``dtypes`` whose rows are contiguous
+    (any row stride)."""
+    if not (t.is_cuda and t.dtype in dtypes and t.dim() == 2 and t.stride(1) == 1):
+        raise ValueError(f"{name}: expected a 2-D device tensor of {dtypes} with contiguous "
+                         f"rows, got {t.dtype} {tuple(t.shape)} strides {t.stride()}")
+    return t.data_ptr()
+
+
+def _opt(t, check, dtypes, name: str) -> int | None:
+    return None if t is None else check(t, dtypes, name)
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -161,8 +187,9 @@ def kvc_store_rows(cache: Cache, rows: torch.Tensor, out_loc: torch.Tensor,
                    status: torch.Tensor | None = None, stream=None) -> None:
     """Quantize bf16 ``rows [n, >=512]`` into ``cache`` at ``out_loc [n]``."""
     d = cache.desc()
-    _check(lib().kvc_store_rows(C.byref(d), rows.data_ptr(), rows.stride(0), out_loc.data_ptr(),
-                                rows.shape[0], _ptr(status), _stream(stream)))
+    _check(lib().kvc_store_rows(C.byref(d), _rows(rows, _B16_T, "rows"), rows.stride(0),
+                                _dense(out_loc, _I32_T, "out_loc"), rows.shape[0],
+                                _opt(status, _dense, _I32_T, "status"), _stream(stream)))
 
 
 def kvc_store_rows_rope(cache: Cache, rows: torch.Tensor, positions: torch.Tensor,
@@ -171,10 +198,11 @@ def kvc_store_rows_rope(cache: Cache, rows: torch.Tensor, positions: torch.Tenso
     """Rotate the rope dims of bf16 ``rows [n, >=512]`` at ``positions [n]``
     (table ``freqs [max_pos, 64]`` fp32) and quantize them at ``out_loc``."""
     d = cache.desc()
-    _check(lib().kvc_store_rows_rope(C.byref(d), rows.data_ptr(), rows.stride(0),
-                                     positions.data_ptr(), freqs.data_ptr(), freqs.shape[0],
-                                     out_loc.data_ptr(), rows.shape[0], _ptr(status),
-                                     _stream(stream)))
+    _check(lib().kvc_store_rows_rope(C.byref(d), _rows(rows, _B16_T, "rows"), rows.stride(0),
+                                     _dense(positions, _I32_T, "positions"),
+                                     _dense(freqs, _F32_T, "freqs"), freqs.shape[0],
+                                     _dense(out_loc, _I32_T, "out_loc"), rows.shape[0],
+                                     _opt(status, _dense, _I32_T, "status"), _stream(stream)))
 
 
 def kvc_dcp_filter_ids(ids: torch.Tensor, token_to_req: torch.Tensor, block_table: torch.Tensor,
@@ -185,12 +213,14 @@ def kvc_dcp_filter_ids(ids: torch.Tensor, token_to_req: torch.Tensor, block_tabl
     """This rank's share of global compressed ids ``[T, k]``: physical slots
     compacted into ``out_slots [T, k]`` (-1 tail), counts into ``out_lens [T]``."""
     T, k = ids.shape
-    _check(lib().kvc_dcp_filter_ids(ids.data_ptr(), T, k, ids.stride(0), token_to_req.data_ptr(),
-                                    block_table.shape[0], block_table.data_ptr(),
-                                    block_table.stride(0), _ptr(valid), page_size, num_pages,
-                                    world, rank, interleave, out_slots.data_ptr(),
-                                    out_slots.stride(0), out_lens.data_ptr(), _ptr(status),
-                                    _stream(stream)))
+    _check(lib().kvc_dcp_filter_ids(_rows(ids, _I32_T, "ids"), T, k, ids.stride(0),
+                                    _dense(token_to_req, _I32_T, "token_to_req"),
+                                    block_table.shape[0], _rows(block_table, _I32_T, "block_table"),
+                                    block_table.stride(0), _opt(valid, _dense, _I32_T, "valid"),
+                                    page_size, num_pages, world, rank, interleave,
+                                    _rows(out_slots, _I32_T, "out_slots"), out_slots.stride(0),
+                                    _dense(out_lens, _I32_T, "out_lens"),
+                                    _opt(status, _dense, _I32_T, "status"), _stream(stream)))
 
 
 def kvc_dequant_gather(cache: Cache, page_table: torch.Tensor | None, ids: torch.Tensor,
@@ -198,9 +228,10 @@ def kvc_dequant_gather(cache: Cache, page_table: torch.Tensor | None, ids: torch
     """``out[j] = bf16 row of ids[j]`` (through ``page_table`` when given)."""
     d = cache.desc()
     n_pages = 0 if page_table is None else page_table.numel()
-    _check(lib().kvc_dequant_gather(C.byref(d), _ptr(page_table), n_pages, ids.data_ptr(),
-                                    ids.numel(), out.data_ptr(), out.stride(0), _ptr(status),
-                                    _stream(stream)))
+    _check(lib().kvc_dequant_gather(C.byref(d), _opt(page_table, _dense, _I32_T, "page_table"),
+                                    n_pages, _dense(ids, _I32_T, "ids"), ids.numel(),
+                                    _rows(out, _B16_T, "out"), out.stride(0),
+                                    _opt(status, _dense, _I32_T, "status"), _stream(stream)))
 
 
 class KVBuf:
@@ -228,10 +259,10 @@ class KVBuf:
         d = cache.desc()
         hit = C.c_int32(0)
         n_pages = 0 if page_table is None else page_table.numel()
-        _check(lib().kvc_dequant_gather_reuse(self._h, C.byref(d), _ptr(page_table), n_pages,
-                                              ids.data_ptr(), ids.numel(), out.data_ptr(),
-                                              out.stride(0), _ptr(status), C.byref(hit),
-                                              _stream(stream)))
+        _check(lib().kvc_dequant_gather_reuse(
+            self._h, C.byref(d), _opt(page_table, _dense, _I32_T, "page_table"), n_pages,
+            _dense(ids, _I32_T, "ids"), ids.numel(), _rows(out, _B16_T, "out"), out.stride(0),
+            _opt(status, _dense, _I32_T, "status"), C.byref(hit), _stream(stream)))
         return bool(hit.value)
 
 
@@ -249,22 +280,25 @@ def kvc_compress_store(*, ratio: int, mode: int, kv: torch.Tensor, score: torch.
     ring_slots, 2, 512]`` bf16 (``[S, 2, 512]`` for one entry)."""
     a = kvc_compress_args()
     a.ratio, a.mode = ratio, mode
-    a.kv, a.kv_stride = kv.data_ptr(), kv.stride(0)
-    a.score = _ptr(score)
+    a.kv, a.kv_stride = _rows(kv, _B16_T, "kv"), kv.stride(0)
+    a.score = _opt(score, _rows, _B16_T, "score")
     a.score_stride = 0 if score is None else score.stride(0)
     a.num_slots = start_pos.numel()
-    a.offsets, a.start_pos = _ptr(offsets), start_pos.data_ptr()
-    a.page_table = _ptr(page_table)
-    a.pt_stride = 0 if page_table is None else page_table.shape[-1]
-    a.out_loc, a.state = _ptr(out_loc), _ptr(state)
-    a.norm_w, a.eps = norm_w.data_ptr(), eps
-    a.freqs, a.max_pos = freqs.data_ptr(), freqs.shape[0]
-    a.latent_out, a.latent_stride = latent_out.data_ptr(), latent_out.stride(0)
+    a.offsets = _opt(offsets, _dense, _I32_T, "offsets")
+    a.start_pos = _dense(start_pos, _I32_T, "start_pos")
+    a.page_table = _opt(page_table, _rows, _I32_T, "page_table")
+    a.pt_stride = 0 if page_table is None else page_table.stride(0)
+    a.out_loc = _opt(out_loc, _dense, _I32_T, "out_loc")
+    a.state = _opt(state, _dense, _B16_T, "state")
+    a.norm_w, a.eps = _dense(norm_w, _B16_T, "norm_w"), eps
+    a.freqs, a.max_pos = _dense(freqs, _F32_T, "freqs"), freqs.shape[0]
+    a.latent_out = _rows(latent_out, _B16_T, "latent_out")
+    a.latent_stride = latent_out.stride(0)
     a.max_out_rows = latent_out.shape[0] if max_out_rows is None else max_out_rows
-    a.prequant_out = _ptr(prequant_out)
+    a.prequant_out = _opt(prequant_out, _rows, _B16_T, "prequant_out")
     a.prequant_stride = 0 if prequant_out is None else prequant_out.stride(0)
     a.cache = cache.desc()
-    a.status = _ptr(status)
+    a.status = _opt(status, _dense, _I32_T, "status")
     a.draft_len, a.ring_slots = draft_len, ring_slots
     a.dcp_world, a.dcp_rank, a.dcp_interleave = dcp_world, dcp_rank, dcp_interleave
     _check(lib().kvc_compress_store(C.byref(a), _stream(stream)))

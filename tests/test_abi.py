@@ -223,3 +223,23 @@ def test_reuse_head_semantics(kvc):
     assert rc == kvc.KVC_EINVAL and hit.value == 0
     assert call(cache=c2, pt=FAKE, out=FAKE + 4096, stride=1024) == 0
     L.kvc_kvbuf_destroy(kb)
+
+
+def test_binding_rejects_host_and_mistyped_tensors(kvc):
+    """The Python binding checks every tensor it passes as a raw pointer
+    (device, dtype, contiguity) before calling the library: host tensors and
+    int64 ids are refused with ValueError, and nothing is launched."""
+    import torch
+    cache = kvc.Cache(torch.zeros((2, 64 * 528), dtype=torch.uint8), "V41", 64)
+    ids = torch.zeros(4, dtype=torch.int32)
+    out = torch.zeros((4, 512), dtype=torch.int16)
+    with pytest.raises(ValueError, match="ids"):
+        kvc.kvc_dequant_gather(cache, None, ids, out)
+    with pytest.raises(ValueError, match="page_table"):
+        kvc.kvc_dequant_gather(cache, torch.zeros(4, dtype=torch.int64), ids, out)
+    with pytest.raises(ValueError, match="rows"):
+        kvc.kvc_store_rows(cache, out, ids)
+    with pytest.raises(ValueError, match="kv"):
+        kvc.kvc_compress_store(ratio=1, mode=kvc.MODE_PREFILL, kv=out, score=None,
+                               start_pos=ids, cache=cache, norm_w=out[0], eps=1e-6,
+                               freqs=torch.zeros((4, 64)), latent_out=out)
