@@ -314,6 +314,22 @@ def test_compress_c3_full(K, layout):
     _check_compress(r, layout, 128, slots, lat)
 
 
+@pytest.mark.parametrize("requests", [128, 256])
+def test_compress_many_requests_full(K, requests):
+    """the C3 batch size (32768 tokens, fused buffer, page 128, V41_FP4) cut
+    into 128 or 256 ragged requests, odd lengths included: the two- and
+    four-slots-per-lane lookups with many items per wave."""
+    _say("compress many requests full", requests)
+    rng = np.random.default_rng(W.BASE_SEED + 30 + requests)
+    lengths = W.ragged_lengths(rng, 32768, requests)
+    case = W.compress_case(W.BASE_SEED + 31 + requests, lengths, ratio=2, page_size=128,
+                           fused=True, state_random=False)
+    r = _run_compress(K, case, "V41_FP4", 2, oracle.PREFILL)
+    lat, slots = _prefill_slots(case, 2)
+    assert r["n_rows"] == int((lengths // 2).sum()) == len(lat)
+    _check_compress(r, "V41_FP4", 128, slots, lat)
+
+
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_compress_ratio1_c2(K, layout):
     """fused ratio-1 compress (norm + rope) of the C2 rows, then a gather of
