@@ -33,7 +33,11 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kLanes;
 constexpr int kMaxPrefillSlots = 8191;   // two LDS tables of S + 1 ints fit in 64 KiB
-constexpr int kTileLog2 = 1;             // default: 2 consecutive compressed rows per work item
+// default rows per prefill work item: 2, or 1 for a batch of at most
+// kSmallBatchRows rows (latent capacity), whose rows then spread over more
+// waves (measured faster up to 8192 rows, slower from 16384)
+constexpr int kTileLog2 = 1;
+constexpr int64_t kSmallBatchRows = 8192;
 
 __device__ __forceinline__ void raise_status(int32_t* status, int32_t bit) {
   if (status != nullptr && lane_id() == 0) atomicOr(status, bit);
@@ -761,7 +765,9 @@ int max_prefill_slots() { return kMaxPrefillSlots; }
 hipError_t launch_compress(const CompressParams& p_in, hipStream_t stream) {
   CompressParams p = p_in;
   // rows per work item: 1, 2 or 4, no more than a page
-  int tl = launch_tuning().compress_tile_log2 >= 0 ? launch_tuning().compress_tile_log2 : kTileLog2;
+  int tl = launch_tuning().compress_tile_log2 >= 0 ? launch_tuning().compress_tile_log2
+           : p.max_out_rows <= kSmallBatchRows        ? 0
+                                                      : kTileLog2;
   tl = tl > 2 ? 2 : tl;
   p.tile_log2 = tl < p.cache.page_bits ? tl : p.cache.page_bits;
   switch (p.cache.layout) {

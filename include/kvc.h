@@ -353,7 +353,8 @@ int kvc_version(void);
 
 /* Launch-shape knob for tuning: the number of workgroups of the gather grid,
  * the cap on the prefill compress grid and the compressed rows one prefill
- * work item takes (1, 2 or 4; 0 = the library's default for each).
+ * work item takes (1, 2 or 4; 0 = the library's default for each -- for the
+ * rows per item, 1 when max_out_rows <= 8192, else 2).
  * Process-wide, not thread-safe; results do not depend on it. */
 int kvc_set_launch_shape(int32_t gather_blocks, int32_t compress_blocks,
                          int32_t compress_tile_rows);
