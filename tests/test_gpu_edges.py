@@ -1,7 +1,7 @@
 """Edge cases of the HIP path against the oracle, through the C ABI: the
 largest prefill batch, the smallest and largest pages, strided buffers,
-ragged gather counts, the longest draft, decode context parallelism at a
-wide group and the widest DCP id rows.  Same bar as the other parity tests
+ragged gather counts, a gather several grid rounds long, the longest draft,
+decode context parallelism at a wide group and the widest DCP id rows.  Same bar as the other parity tests
 (bytes bit-exact; fused outputs within the stated tolerance)."""
 import numpy as np
 import pytest
@@ -149,6 +149,32 @@ def test_gather_ragged_counts(K, n, layout):
     torch.cuda.synchronize()
     g = host(out, np.uint16)
     assert st == 0 and np.array_equal(g[:n], want) and np.all(g[n] == 9)
+
+
+def test_gather_grid_stride_sampled(K):
+    """3,000,017 ids (random, 1% of them -1) from a 262,144-row V41 cache into
+    a 3 GB output: past the gather grid's one-round capacity of 2^20 ids, so
+    every wave takes about three batches and the last batch is ragged.  The
+    first and last 256 rows and 8192 sampled rows are compared with the
+    oracle; the guard row after the output is untouched."""
+    _say("gather grid stride", 3000017)
+    n = 3000017
+    c = W.gather_case(W.BASE_SEED + 40, 4096, 64, 1, 528, 512, 16)
+    rng = np.random.default_rng(W.BASE_SEED + 41)
+    ids = rng.integers(0, 4096 * 64, size=n).astype(np.int32)
+    ids[rng.random(n) < 0.01] = -1
+    out = torch.full((n + 1, 512), 9, dtype=torch.int16, device="cuda")
+    s = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvc_dequant_gather(K.Cache(dev(c["cache"]), "V41", 64), dev(c["page_table"]), dev(ids),
+                         out[:n], s)
+    pick = np.unique(np.concatenate([np.arange(256), np.arange(n - 256, n),
+                                     rng.integers(0, n, size=8192)]))
+    got = out[torch.from_numpy(pick).cuda()].cpu().numpy().view(np.uint16)
+    want, st = oracle.dequant_gather(c["cache"], "V41", 64, c["page_table"], ids[pick])
+    assert st == 0 and int(s.item()) == 0
+    assert np.array_equal(got, want)
+    assert np.all(out[n].cpu().numpy() == 9)
+    del out
 
 
 def test_verify_longest_draft(K):
