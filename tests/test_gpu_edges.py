@@ -1,8 +1,9 @@
 """Edge cases of the HIP path against the oracle, through the C ABI: the
 largest prefill batch, the smallest and largest pages, strided buffers,
-ragged gather counts, a gather several grid rounds long, the longest draft,
-decode context parallelism at a wide group and the widest DCP id rows.  Same bar as the other parity tests
-(bytes bit-exact; fused outputs within the stated tolerance)."""
+ragged gather counts, a gather and stores several grid rounds long, the
+longest draft, decode context parallelism at a wide group and the widest
+DCP id rows.  Same bar as the other parity tests (bytes bit-exact; fused
+outputs within the stated tolerance)."""
 import numpy as np
 import pytest
 import torch
@@ -175,6 +176,39 @@ def test_gather_grid_stride_sampled(K):
     assert np.array_equal(got, want)
     assert np.all(out[n].cpu().numpy() == 9)
     del out
+
+
+@pytest.mark.parametrize("layout,rope", [("V41_FP4", False), ("V41", True)])
+def test_store_grid_stride(K, layout, rope):
+    """200,003 rows into one cache: past the store grid's one-round capacity
+    of 65,536 rows, so every wave takes about three trips and the last one is
+    ragged; N(0, 1) rows, 1% padded (out_loc 0).  Plain store and RoPE store
+    (positions across a 65,536-entry table): every cache byte equals the
+    oracle's."""
+    _say("store grid stride", layout, rope)
+    n, ps = 200003, 64
+    rng = np.random.default_rng(W.BASE_SEED + 42 + rope)
+    rows = W.normal_bf16(rng, (n, 512))
+    pages = n // ps + 3
+    loc = (W.random_pages(rng, pages - 1, pages).astype(np.int64)[:, None] * ps
+           + np.arange(ps)[None, :]).reshape(-1)[:n]
+    loc = rng.permutation(loc).astype(np.int32)
+    loc[rng.random(n) < 0.01] = 0
+    rb = oracle.layout_bytes(layout)[2]
+    hc = np.full((pages, ps * rb), 0x3C, np.uint8)
+    dc = dev(hc)
+    s = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if rope:
+        pos = rng.integers(0, 65536, size=n).astype(np.int32)
+        fr = W.rope_freqs(65536)
+        _, st = oracle.store_rows_rope(hc, layout, ps, rows, pos, fr, loc)
+        K.kvc_store_rows_rope(K.Cache(dc, layout, ps), dev(rows), dev(pos), dev(fr), dev(loc), s)
+    else:
+        st = oracle.store_rows(hc, layout, ps, rows, loc)
+        K.kvc_store_rows(K.Cache(dc, layout, ps), dev(rows), dev(loc), s)
+    torch.cuda.synchronize()
+    assert st == 0 and int(s.item()) == 0
+    assert np.array_equal(host(dc), hc)
 
 
 def test_verify_longest_draft(K):
