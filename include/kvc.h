@@ -328,8 +328,10 @@ int kvc_dcp_filter_ids(const int32_t* ids, int64_t T, int32_t k, int64_t ids_str
  * page table, n_pages, ids pointer, n, output pointer, output stride), in
  * which case it launches nothing and sets *hit = 1.  The key compares
  * pointers, not contents: the caller must not rewrite the ids, the page
- * table or the cache rows behind a head it still relies on; that is what
- * kvc_kvbuf_forget / kvc_kvbuf_begin_forward are for.
+ * table, the cache rows or the output behind a head it still relies on;
+ * that is what kvc_kvbuf_forget / kvc_kvbuf_begin_forward are for.  A hit
+ * launches nothing, so a reader on another stream must still be ordered
+ * after the gather that filled the output.
  *   kvc_kvbuf_forget         a plain get or a reallocation: drop the head
  *   kvc_kvbuf_begin_forward  a new forward pass: drop the head
  * A kvc_kvbuf is not thread-safe; it owns no device memory. */
