@@ -423,6 +423,105 @@ def test_prefill_compress_graph_replay(K):
                 assert_latent_close(replay[1].view(np.uint16)[:n], lat_o)
 
 
+def test_hot_path_graph_replay(K):
+    """One step of the path captured in a graph: the prefill compressor, then
+    a dequant-gather by physical slot that reads rows the compressor has just
+    written (and some it has not, and -1 ids).  Inputs and ids are refreshed
+    in place between replays, with eager work between them: every replay
+    equals eager calls on the same inputs, bit for bit."""
+    layout, ps, S, T, n_ids = "V41", 16, 6, 500, 700
+    cases = [W.compress_case(600 + i, W.ragged_lengths(np.random.default_rng(610 + i), T - 30, S),
+                             ratio=2, page_size=ps, fused=True, pt_slack=2) for i in range(3)]
+    rb = oracle.layout_bytes(layout)[2]
+    npg = max(c["num_pages"] for c in cases)
+    pts = max(c["page_table"].shape[1] for c in cases)
+    proj = torch.zeros((T, 1024), dtype=torch.int16, device="cuda")
+    offs = torch.zeros((2, S), dtype=torch.int32, device="cuda")
+    start = torch.zeros(S, dtype=torch.int32, device="cuda")
+    pt = torch.zeros((S, pts), dtype=torch.int32, device="cuda")
+    state = torch.zeros((S, 2, 512), dtype=torch.int16, device="cuda")
+    cache = torch.zeros((npg, ps * rb), dtype=torch.uint8, device="cuda")
+    lat = torch.zeros((T // 2 + S, 512), dtype=torch.int16, device="cuda")
+    ids = torch.zeros(n_ids, dtype=torch.int32, device="cuda")
+    out = torch.zeros((n_ids, 512), dtype=torch.int16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    w = dev(cases[0]["norm_w"])
+    fr = dev(W.rope_freqs(T + 64))
+
+    def load(i, c):
+        proj.zero_()
+        proj[:c["kv"].shape[0]].copy_(dev(c["kv"]))
+        offs.copy_(dev(c["offsets"]))
+        start.copy_(dev(c["start_pos"]))
+        pt.zero_()
+        pt[:, :c["page_table"].shape[1]].copy_(dev(c["page_table"]))
+        state.copy_(dev(c["state"]))
+        cache.fill_(0x11)
+        lat.zero_()
+        out.fill_(7)
+        # slots the compressor writes, other slots, and -1
+        _, slots = _prefill_slots_of(c)
+        rng = np.random.default_rng(620 + i)
+        pick = np.concatenate([rng.choice(slots, size=n_ids // 2),
+                               rng.integers(0, npg * ps, size=n_ids - n_ids // 2)])
+        pick[rng.random(n_ids) < 0.05] = -1
+        ids.copy_(torch.from_numpy(rng.permutation(pick).astype(np.int32)))
+
+    def step():
+        status.zero_()
+        K.kvc_compress_store(ratio=2, mode=K.MODE_PREFILL, kv=proj[:, :512], score=proj[:, 512:],
+                             start_pos=start, cache=K.Cache(cache, layout, ps), norm_w=w,
+                             eps=1e-6, freqs=fr, latent_out=lat, offsets=offs, page_table=pt,
+                             state=state, status=status)
+        K.kvc_dequant_gather(K.Cache(cache, layout, ps), None, ids, out, status)
+
+    def snap():
+        return [host(t).copy() for t in (cache, lat, state, out, status)]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        load(0, cases[0])
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, c in enumerate(cases):
+            _say("hot path graph replay", rep, i)
+            load(i, c)
+            torch.cuda.synchronize()
+            step()
+            torch.cuda.synchronize()
+            eager = snap()
+            load(i, c)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            replay = snap()
+            assert int(eager[4][0]) == 0
+            for a, b in zip(eager, replay):
+                assert np.array_equal(a, b), (rep, i)
+
+
+def _prefill_slots_of(c):
+    """(latent rows, cache slots) of a ratio-2 prefill case, in emission order."""
+    lat, slots, L = [], [], 0
+    ps = c["page_size"]
+    for b in range(c["S"]):
+        n, p0 = int(c["offsets"][1, b]), int(c["start_pos"][b])
+        for q in range(p0, p0 + max(n, 0)):
+            if q % 2 == 1:
+                cc = q // 2
+                slots.append(int(c["page_table"][b, cc // ps]) * ps + cc % ps)
+                lat.append(L)
+                L += 1
+    return lat, slots
+
+
 # ================================================================= quantizer, exhaustive
 def _groups_to_rows(groups, gsize):
     """pack groups of gsize bf16 values into 512-dim rows (zero padded)."""
