@@ -275,8 +275,12 @@ __device__ __forceinline__ uint4 decode_lane<kV4>(const LaneCodes<kV4>& c, int l
 // any store.  32-id batches give 8192 waves for 262,144 ids, about one
 // resident round of the chip (measured faster than 16, 48 or 64); a smaller
 // gather takes smaller batches, so that its rows spread over more waves.
+// Eight waves per SIMD asked of the compiler: it then keeps the kernel to 78
+// scalar registers (93 otherwise), and the launch's 8192 waves go through
+// 0.9% faster.
 template <int L>
-__global__ __launch_bounds__(kBlock) void dequant_gather_kernel(GatherParams p) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void dequant_gather_kernel(GatherParams p) {
   const PagedKV<L> kv = paged<L>(p.cache);
   const int lane = lane_id();
   const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
