@@ -39,10 +39,6 @@ constexpr int kMaxPrefillSlots = 8191;   // two LDS tables of S + 1 ints fit in 
 constexpr int kTileLog2 = 1;
 constexpr int64_t kSmallBatchRows = 8192;
 
-__device__ __forceinline__ void raise_status(int32_t* status, int32_t bit) {
-  if (status != nullptr && lane_id() == 0) atomicOr(status, bit);
-}
-
 // One compressed row.  Token rows are indices into the projection buffer;
 // `from_state` says the pair's first token is the pending-state entry
 // `st_row` (entries counted over all slots: slot b's ring starts at entry

@@ -22,10 +22,6 @@ __device__ __forceinline__ PagedKV<L> paged(const CacheView& c) {
   return PagedKV<L>{c.base, c.page_stride, c.num_pages, c.page_bits};
 }
 
-__device__ __forceinline__ void raise_status(int32_t* status, int32_t bit) {
-  if (status != nullptr && lane_id() == 0) atomicOr(status, bit);
-}
-
 // ------------------------------------------------------------------ store
 // A wave stores kStoreRows rows per loop trip: the loads of all of them (row
 // bytes, destination, position) are issued before the first is quantized, so

@@ -66,6 +66,11 @@ __device__ __forceinline__ uint32_t pack4_bytes_shr(uint32_t v) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// set `bit` in the optional device status word (lane 0 of the wave)
+__device__ __forceinline__ void raise_status(int32_t* status, int32_t bit) {
+  if (status != nullptr && lane_id() == 0) atomicOr(status, bit);
+}
+
 // Load from memory that no thread writes while the kernel runs (the caller's
 // read-only inputs: offsets, positions, page tables, ids).  Going through the
 // constant address space lets the compiler use a scalar load when the address
