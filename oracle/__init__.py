@@ -22,7 +22,7 @@ _LIB_PATH = os.path.join(HERE, "libkvc_oracle.so")
 LAYOUTS = {"V4": 0, "V41": 1, "V41_FP4": 2}
 PREFILL, DECODE, VERIFY = 0, 1, 2
 ST_ID_RANGE, ST_PAGE_RANGE, ST_PT_RANGE, ST_LATENT_RANGE, ST_POS_RANGE = 1, 2, 4, 8, 16
-ST_REQ_RANGE = 32
+ST_REQ_RANGE, ST_TOKEN_RANGE = 32, 64
 
 _lib = None
 
@@ -48,6 +48,7 @@ class _CompressArgs(C.Structure):
         ("cache", _Cache), ("status", C.c_void_p),
         ("draft_len", C.c_int32), ("ring_slots", C.c_int32),
         ("dcp_world", C.c_int32), ("dcp_rank", C.c_int32), ("dcp_interleave", C.c_int32),
+        ("kv_rows", C.c_int64),
     ]
 
 
@@ -318,6 +319,9 @@ def compress(*, ratio, mode, kv, score=None, fused=False, offsets=None, start_po
     a.status = _p(st)
     a.draft_len, a.ring_slots = draft_len, ring_slots
     a.dcp_world, a.dcp_rank, a.dcp_interleave = dcp_world, dcp_rank, dcp_interleave
+    a.kv_rows = kv.shape[0] if score is None or fused else min(kv.shape[0], score.shape[0])
+    if mode != PREFILL:
+        assert a.kv_rows >= S * (draft_len if mode == VERIFY else 1), "token rows"
     n_rows = lib().kvo_count_rows(C.byref(a))
     if max_out_rows is None:
         max_out_rows = n_rows if mode == PREFILL else S * (draft_len if mode == VERIFY else 1)

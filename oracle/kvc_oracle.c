@@ -560,6 +560,13 @@ static int64_t build_plan(const kvo_compress_args* a, kvo_row* rows,
     if (a->mode == KVO_PREFILL) {
       int64_t first = a->offsets[b], n = a->offsets[S + b], P = a->start_pos[b];
       if (n <= 0 || P < 0) continue;
+      /* reading: a slot whose extend rows are not all inside the projection
+       * buffer is skipped whole and flagged (the pages index the buffer with
+       * the offsets and give no rule for rows outside it) */
+      if (first < 0 || first + n > a->kv_rows) {
+        if (rows) set_status(a->status, KVO_ST_TOKEN_RANGE);
+        continue;
+      }
       if (a->ratio == 1) {
         for (int64_t t = 0; t < n; ++t) {
           if (rows) {

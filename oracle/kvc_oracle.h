@@ -55,7 +55,8 @@ enum {
   KVO_ST_PT_RANGE = 4,      /* compressed row beyond the slot's page table */
   KVO_ST_LATENT_RANGE = 8,  /* latent ordinal beyond the output capacity   */
   KVO_ST_POS_RANGE = 16,    /* rotary position outside the table           */
-  KVO_ST_REQ_RANGE = 32     /* request index outside the block table       */
+  KVO_ST_REQ_RANGE = 32,    /* request index outside the block table       */
+  KVO_ST_TOKEN_RANGE = 64   /* prefill slot's token rows outside the buffer */
 };
 
 typedef struct {
@@ -97,6 +98,7 @@ typedef struct {
   int32_t dcp_world;          /* context-parallel ranks (<= 1: none) */
   int32_t dcp_rank;
   int32_t dcp_interleave;     /* consecutive compressed rows per rank turn */
+  int64_t kv_rows;            /* token rows the kv / score buffers hold */
 } kvo_compress_args;
 
 /* layouts */
