@@ -348,9 +348,6 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the verify / RoPE-store / DCP-filter / graph-replay / reuse measurements")
-    ap.add_argument("--gather-blocks", type=int, default=0)
-    ap.add_argument("--compress-blocks", type=int, default=0)
-    ap.add_argument("--compress-tile-rows", type=int, default=0)
     ap.add_argument("--sweep", action="store_true",
                     help="only measure compress and gather throughput at several sizes, one "
                          "JSON line per size, and exit")
@@ -380,7 +377,6 @@ def main() -> int:
         print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
                           "launches": 5}), flush=True)
         return 0
-    kvc.kvc_set_launch_shape(args.gather_blocks, args.compress_blocks, args.compress_tile_rows)
     if args.sweep:
         def d(a):
             a = np.ascontiguousarray(a)

@@ -26,6 +26,7 @@ LAYOUTS = {"V4": LAYOUT_V4, "V41": LAYOUT_V41, "V41_FP4": LAYOUT_V41_FP4}
 MODE_PREFILL, MODE_DECODE, MODE_VERIFY = 0, 1, 2
 STATUS_ID_RANGE, STATUS_PAGE_RANGE, STATUS_PT_RANGE = 1, 2, 4
 STATUS_LATENT_RANGE, STATUS_POS_RANGE, STATUS_REQ_RANGE = 8, 16, 32
+STATUS_TOKEN_RANGE = 64
 
 
 class KvcError(RuntimeError):
@@ -60,6 +61,7 @@ class kvc_compress_args(C.Structure):
         ("cache", kvc_cache), ("status", C.c_void_p),
         ("draft_len", C.c_int32), ("ring_slots", C.c_int32),
         ("dcp_world", C.c_int32), ("dcp_rank", C.c_int32), ("dcp_interleave", C.c_int32),
+        ("tile_rows", C.c_int32), ("kv_rows", C.c_int64), ("pt_width", C.c_int64),
     ]
 
 
@@ -70,8 +72,8 @@ SIGNATURES = {
     "kvc_store_rows": (C.c_int, [C.POINTER(kvc_cache), _VP, _I64, _VP, _I64, _VP, _VP]),
     "kvc_store_rows_rope": (C.c_int, [C.POINTER(kvc_cache), _VP, _I64, _VP, _VP, _I64, _VP, _I64,
                                       _VP, _VP]),
-    "kvc_dcp_filter_ids": (C.c_int, [_VP, _I64, _I32, _I64, _VP, _I32, _VP, _I64, _VP, _I32, _I64,
-                                     _I32, _I32, _I32, _VP, _I64, _VP, _VP, _VP]),
+    "kvc_dcp_filter_ids": (C.c_int, [_VP, _I64, _I32, _I64, _VP, _I32, _VP, _I64, _I64, _VP, _I32,
+                                     _I64, _I32, _I32, _I32, _VP, _I64, _VP, _VP, _VP]),
     "kvc_compress_store": (C.c_int, [C.POINTER(kvc_compress_args), _VP]),
     "kvc_dequant_gather": (C.c_int, [C.POINTER(kvc_cache), _VP, _I64, _VP, _I64, _VP, _I64, _VP, _VP]),
     "kvc_kvbuf_create": (_VP, []),
@@ -82,7 +84,6 @@ SIGNATURES = {
                                            _I64, _VP, _VP, _VP]),
     "kvc_last_error": (C.c_char_p, []),
     "kvc_version": (C.c_int, []),
-    "kvc_set_launch_shape": (C.c_int, [_I32, _I32, _I32]),
 }
 
 _lib = None
@@ -142,6 +143,20 @@ def _opt(t, check, dtypes, name: str) -> int | None:
     return None if t is None else check(t, dtypes, name)
 
 
+def _need(ok: bool, msg: str) -> None:
+    """A size the library would trust (it reads or writes that many entries)
+    that the tensor does not have: refused before anything is launched."""
+    if not ok:
+        raise ValueError(msg)
+
+
+def _rows_of(t, name: str, min_cols: int = 512) -> int:
+    """Row count of a 2-D row buffer holding at least ``min_cols`` columns."""
+    _need(t.dim() == 2, f"{name}: expected a 2-D tensor, got shape {tuple(t.shape)}")
+    _need(t.shape[1] >= min_cols, f"{name}: rows hold {t.shape[1]} columns, need {min_cols}")
+    return t.shape[0]
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -178,14 +193,11 @@ def kvc_layout_query(layout) -> kvc_layout_info:
     return info
 
 
-def kvc_set_launch_shape(gather_blocks: int = 0, compress_blocks: int = 0,
-                         compress_tile_rows: int = 0) -> None:
-    _check(lib().kvc_set_launch_shape(gather_blocks, compress_blocks, compress_tile_rows))
-
-
 def kvc_store_rows(cache: Cache, rows: torch.Tensor, out_loc: torch.Tensor,
                    status: torch.Tensor | None = None, stream=None) -> None:
     """Quantize bf16 ``rows [n, >=512]`` into ``cache`` at ``out_loc [n]``."""
+    n = _rows_of(rows, "rows")
+    _need(out_loc.numel() >= n, f"out_loc: {out_loc.numel()} entries for {n} rows")
     d = cache.desc()
     _check(lib().kvc_store_rows(C.byref(d), _rows(rows, _B16_T, "rows"), rows.stride(0),
                                 _dense(out_loc, _I32_T, "out_loc"), rows.shape[0],
@@ -197,6 +209,11 @@ def kvc_store_rows_rope(cache: Cache, rows: torch.Tensor, positions: torch.Tenso
                         status: torch.Tensor | None = None, stream=None) -> None:
     """Rotate the rope dims of bf16 ``rows [n, >=512]`` at ``positions [n]``
     (table ``freqs [max_pos, 64]`` fp32) and quantize them at ``out_loc``."""
+    n = _rows_of(rows, "rows")
+    _need(out_loc.numel() >= n, f"out_loc: {out_loc.numel()} entries for {n} rows")
+    _need(positions.numel() >= n, f"positions: {positions.numel()} entries for {n} rows")
+    _need(freqs.dim() == 2 and freqs.shape[1] == 64, f"freqs: shape {tuple(freqs.shape)}, "
+                                                     "expected [max_pos, 64]")
     d = cache.desc()
     _check(lib().kvc_store_rows_rope(C.byref(d), _rows(rows, _B16_T, "rows"), rows.stride(0),
                                      _dense(positions, _I32_T, "positions"),
@@ -212,11 +229,20 @@ def kvc_dcp_filter_ids(ids: torch.Tensor, token_to_req: torch.Tensor, block_tabl
                        stream=None) -> None:
     """This rank's share of global compressed ids ``[T, k]``: physical slots
     compacted into ``out_slots [T, k]`` (-1 tail), counts into ``out_lens [T]``."""
+    _need(ids.dim() == 2, f"ids: expected [T, k], got shape {tuple(ids.shape)}")
     T, k = ids.shape
+    _need(token_to_req.numel() >= T, f"token_to_req: {token_to_req.numel()} entries for {T} rows")
+    _need(valid is None or valid.numel() >= T, f"valid: fewer than {T} entries")
+    _need(out_slots.dim() == 2 and out_slots.shape[0] >= T and out_slots.shape[1] >= k,
+          f"out_slots: shape {tuple(out_slots.shape)}, need at least [{T}, {k}]")
+    _need(out_lens.numel() >= T, f"out_lens: {out_lens.numel()} entries for {T} rows")
+    _need(block_table.dim() == 2, f"block_table: expected [n_req, pages], got "
+                                  f"{tuple(block_table.shape)}")
     _check(lib().kvc_dcp_filter_ids(_rows(ids, _I32_T, "ids"), T, k, ids.stride(0),
                                     _dense(token_to_req, _I32_T, "token_to_req"),
                                     block_table.shape[0], _rows(block_table, _I32_T, "block_table"),
-                                    block_table.stride(0), _opt(valid, _dense, _I32_T, "valid"),
+                                    block_table.stride(0), block_table.shape[1],
+                                    _opt(valid, _dense, _I32_T, "valid"),
                                     page_size, num_pages, world, rank, interleave,
                                     _rows(out_slots, _I32_T, "out_slots"), out_slots.stride(0),
                                     _dense(out_lens, _I32_T, "out_lens"),
@@ -226,6 +252,7 @@ def kvc_dcp_filter_ids(ids: torch.Tensor, token_to_req: torch.Tensor, block_tabl
 def kvc_dequant_gather(cache: Cache, page_table: torch.Tensor | None, ids: torch.Tensor,
                        out: torch.Tensor, status: torch.Tensor | None = None, stream=None) -> None:
     """``out[j] = bf16 row of ids[j]`` (through ``page_table`` when given)."""
+    _need(_rows_of(out, "out") >= ids.numel(), f"out: {out.shape[0]} rows for {ids.numel()} ids")
     d = cache.desc()
     n_pages = 0 if page_table is None else page_table.numel()
     _check(lib().kvc_dequant_gather(C.byref(d), _opt(page_table, _dense, _I32_T, "page_table"),
@@ -256,6 +283,8 @@ class KVBuf:
 
     def kvc_dequant_gather_reuse(self, cache: Cache, page_table, ids, out, status=None,
                                  stream=None) -> bool:
+        _need(_rows_of(out, "out") >= ids.numel(),
+              f"out: {out.shape[0]} rows for {ids.numel()} ids")
         d = cache.desc()
         hit = C.c_int32(0)
         n_pages = 0 if page_table is None else page_table.numel()
@@ -273,32 +302,69 @@ def kvc_compress_store(*, ratio: int, mode: int, kv: torch.Tensor, score: torch.
                        out_loc: torch.Tensor | None = None, state: torch.Tensor | None = None,
                        prequant_out: torch.Tensor | None = None, status: torch.Tensor | None = None,
                        draft_len: int = 1, ring_slots: int = 1, dcp_world: int = 1,
-                       dcp_rank: int = 0, dcp_interleave: int = 1, stream=None) -> None:
+                       dcp_rank: int = 0, dcp_interleave: int = 1, tile_rows: int = 0,
+                       stream=None) -> None:
     """The fused compressor.  ``kv``/``score`` are 2-D views whose row stride
     is passed through (a fused ``|kv|score|`` buffer ``proj [T, 1024]`` is
     ``kv=proj[:, :512], score=proj[:, 512:]``).  ``state`` is ``[S,
-    ring_slots, 2, 512]`` bf16 (``[S, 2, 512]`` for one entry)."""
+    ring_slots, 2, 512]`` bf16 (``[S, 2, 512]`` for one entry).  A page
+    table may be a column slice of a wider table: its width bounds the
+    logical pages, its row stride addresses the rows."""
+    S = start_pos.numel()
+    D = draft_len if mode == MODE_VERIFY else 1
+    kv_rows = _rows_of(kv, "kv")
+    if score is not None:
+        kv_rows = min(kv_rows, _rows_of(score, "score"))
+    lat_rows = _rows_of(latent_out, "latent_out")
+    if max_out_rows is None:
+        max_out_rows = lat_rows
+    _need(0 <= max_out_rows <= lat_rows,
+          f"max_out_rows {max_out_rows}: latent_out holds {lat_rows} rows")
+    _need(prequant_out is None or _rows_of(prequant_out, "prequant_out") >= max_out_rows,
+          f"prequant_out: fewer than max_out_rows = {max_out_rows} rows")
+    if mode != MODE_PREFILL:
+        _need(max_out_rows >= S * D, f"max_out_rows {max_out_rows}: decode / verify write "
+                                     f"latent rows up to {S * D}")
+        _need(kv_rows >= S * D, f"kv: {kv_rows} token rows for {S} slots x {D} tokens")
+        _need(out_loc is None or out_loc.numel() >= S * D,
+              f"out_loc: {out_loc.numel() if out_loc is not None else 0} entries for {S * D} "
+              "tokens")
+    else:
+        _need(offsets is not None and offsets.numel() >= 2 * S,
+              f"offsets: expected [2, {S}] entries")
+    if page_table is not None:
+        _need(page_table.dim() == 2 and page_table.shape[0] >= S,
+              f"page_table: shape {tuple(page_table.shape)}, need {S} rows")
+    if ratio == 2:
+        _need(state is not None and state.numel() >= S * max(ring_slots, 1) * 1024,
+              f"state: need [{S}, {max(ring_slots, 1)}, 2, 512] bf16")
+    _need(norm_w.numel() >= 512, "norm_w: expected 512 entries")
+    _need(freqs.dim() == 2 and freqs.shape[1] == 64,
+          f"freqs: shape {tuple(freqs.shape)}, expected [max_pos, 64]")
     a = kvc_compress_args()
     a.ratio, a.mode = ratio, mode
     a.kv, a.kv_stride = _rows(kv, _B16_T, "kv"), kv.stride(0)
     a.score = _opt(score, _rows, _B16_T, "score")
     a.score_stride = 0 if score is None else score.stride(0)
-    a.num_slots = start_pos.numel()
+    a.num_slots = S
+    a.kv_rows = kv_rows
     a.offsets = _opt(offsets, _dense, _I32_T, "offsets")
     a.start_pos = _dense(start_pos, _I32_T, "start_pos")
     a.page_table = _opt(page_table, _rows, _I32_T, "page_table")
     a.pt_stride = 0 if page_table is None else page_table.stride(0)
+    a.pt_width = 0 if page_table is None else page_table.shape[1]
     a.out_loc = _opt(out_loc, _dense, _I32_T, "out_loc")
     a.state = _opt(state, _dense, _B16_T, "state")
     a.norm_w, a.eps = _dense(norm_w, _B16_T, "norm_w"), eps
     a.freqs, a.max_pos = _dense(freqs, _F32_T, "freqs"), freqs.shape[0]
     a.latent_out = _rows(latent_out, _B16_T, "latent_out")
     a.latent_stride = latent_out.stride(0)
-    a.max_out_rows = latent_out.shape[0] if max_out_rows is None else max_out_rows
+    a.max_out_rows = max_out_rows
     a.prequant_out = _opt(prequant_out, _rows, _B16_T, "prequant_out")
     a.prequant_stride = 0 if prequant_out is None else prequant_out.stride(0)
     a.cache = cache.desc()
     a.status = _opt(status, _dense, _I32_T, "status")
     a.draft_len, a.ring_slots = draft_len, ring_slots
     a.dcp_world, a.dcp_rank, a.dcp_interleave = dcp_world, dcp_rank, dcp_interleave
+    a.tile_rows = tile_rows
     _check(lib().kvc_compress_store(C.byref(a), _stream(stream)))

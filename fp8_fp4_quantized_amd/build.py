@@ -1,7 +1,9 @@
-"""Build ``libkvc.so`` (the HIP library behind include/kvc.h) for gfx950.
+"""Build ``libkvc.so`` (the HIP library behind include/kvc.h) and
+``libkvc_ceiling.so`` (the benchmark's streaming yardstick,
+include/kvc_ceiling.h) for gfx950.
 
 Every HIP source is compiled with hipcc for ``--offload-arch=gfx950`` and
-linked into one shared library next to this file.  Packed fp32 VALU forms are
+linked into shared libraries next to this file.  Packed fp32 VALU forms are
 switched off (``-packed-fp32-ops``): the kernels' float arithmetic stays on
 the scalar-per-lane instructions.
 """
@@ -16,6 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvc.so")
 SOURCES = ["kvc_api.cpp", "store_gather.hip", "compress.hip"]
+CEILING_LIB = os.path.join(HERE, "libkvc_ceiling.so")
+CEILING_SOURCES = ["ceiling.hip"]
 ARCH = "gfx950"
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -36,18 +40,24 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    objdir = os.path.join(HERE, "_build")
-    os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(SOURCES, objs)))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    every = SOURCES + CEILING_SOURCES
+    objs = {s: os.path.join(objdir, s.rsplit(".", 1)[0] + ".o") for s in every}
+    with cf.ThreadPoolExecutor(max_workers=len(every)) as ex:
+        list(ex.map(lambda s: _compile(s, objs[s], verbose), every))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in CEILING_SOURCES], CEILING_LIB, verbose)
     return LIB
 
 

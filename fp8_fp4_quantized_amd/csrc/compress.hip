@@ -38,6 +38,9 @@ constexpr int kMaxPrefillSlots = 8191;   // two LDS tables of S + 1 ints fit in 
 // waves (measured faster up to 8192 rows, slower from 16384)
 constexpr int kTileLog2 = 1;
 constexpr int64_t kSmallBatchRows = 8192;
+// prefill grid cap: 1024 workgroups of 4 waves (measured best for the
+// 32,768-token batch against 512 .. 2048)
+constexpr int64_t kMaxPrefillBlocks = 1024;
 
 // One compressed row.  Token rows are indices into the projection buffer;
 // `from_state` says the pair's first token is the pending-state entry
@@ -226,7 +229,7 @@ __device__ __forceinline__ void page_loc(const CompressParams& p, int32_t b, int
   loc = 0;
   err = 0;
   const int32_t lp = c >> p.cache.page_bits;
-  if (lp >= p.pt_stride) {
+  if (lp >= p.pt_width) {
     err = kStPtRange;
     return;
   }
@@ -312,6 +315,13 @@ __device__ __forceinline__ SlotWork slot_work(int32_t n, int32_t P, int32_t tile
   return s;
 }
 
+// a slot's token rows first .. first + n - 1 lie in the projection buffer
+// (a slot with no tokens is always in range); a slot outside it is skipped
+// whole and flagged
+__device__ __forceinline__ bool slot_in_buffer(int32_t first, int32_t n, int64_t kv_rows) {
+  return n <= 0 || (first >= 0 && (int64_t)first + n <= kv_rows);
+}
+
 // exclusive scans of work items and rows over the slots, into LDS
 template <int RATIO>
 __device__ void build_tables(const CompressParams& p, int32_t* item_start, int32_t* row_start) {
@@ -322,7 +332,12 @@ __device__ void build_tables(const CompressParams& p, int32_t* item_start, int32
   for (int base = 0; base < S; base += kBlock) {
     const int b = base + threadIdx.x;
     SlotWork sw{0, 0, 0, false};
-    if (b < S) sw = slot_work<RATIO>(p.offsets[S + b], p.start_pos[b], p.tile_log2);
+    if (b < S) {
+      const int32_t n = p.offsets[S + b];
+      const bool in_buf = slot_in_buffer(p.offsets[b], n, p.kv_rows);
+      if (!in_buf && blockIdx.x == 0 && p.status != nullptr) atomicOr(p.status, kStTokenRange);
+      sw = slot_work<RATIO>(in_buf ? n : 0, p.start_pos[b], p.tile_log2);
+    }
     int32_t si = sw.items, sr = sw.rows;
 #pragma unroll
     for (int d = 1; d < kLanes; d <<= 1) {
@@ -446,6 +461,10 @@ __global__ __launch_bounds__(kBlock) void compress_prefill_small_kernel(Compress
     P = p.start_pos[lane];
   }
   const uint4 wr = ld_u4(p.norm_w + kDimsPerLane * lane);
+  if (!slot_in_buffer(first, n, p.kv_rows)) {
+    n = 0;
+    if (blockIdx.x == 0 && p.status != nullptr) atomicOr(p.status, kStTokenRange);
+  }
   const SlotWork sw = lane < S ? slot_work<RATIO>(n, P, p.tile_log2) : SlotWork{0, 0, 0, false};
   int32_t inc_i = sw.items, inc_r = sw.rows;
 #pragma unroll
@@ -494,6 +513,13 @@ __global__ __launch_bounds__(kBlock) void compress_prefill_multi_kernel(Compress
     }
   }
   const uint4 wr = ld_u4(p.norm_w + kDimsPerLane * lane);
+#pragma unroll
+  for (int k = 0; k < SPL; ++k) {
+    if (!slot_in_buffer(first[k], n[k], p.kv_rows)) {
+      n[k] = 0;
+      if (blockIdx.x == 0 && p.status != nullptr) atomicOr(p.status, kStTokenRange);
+    }
+  }
   int32_t tot_i = 0, tot_r = 0;
 #pragma unroll
   for (int k = 0; k < SPL; ++k) {
@@ -708,8 +734,7 @@ hipError_t launch_one(const CompressParams& p, hipStream_t stream) {
     // up to two partial tiles (or one tail item) per slot
     const int64_t items_hint = (p.max_out_rows >> p.tile_log2) + 2 * (int64_t)p.num_slots + 1;
     int64_t blocks = (items_hint + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int cap = launch_tuning().compress_blocks > 0 ? launch_tuning().compress_blocks : 1024;
-    if (blocks > cap) blocks = cap;
+    if (blocks > kMaxPrefillBlocks) blocks = kMaxPrefillBlocks;
     if (blocks < 1) blocks = 1;
     const size_t lds = sizeof(int32_t) * 2 * (size_t)(p.num_slots + 1);
     // up to 256 slots: slot lookup by ballots over 1, 2 or 4 slots per lane
@@ -761,11 +786,10 @@ int max_prefill_slots() { return kMaxPrefillSlots; }
 
 hipError_t launch_compress(const CompressParams& p_in, hipStream_t stream) {
   CompressParams p = p_in;
-  // rows per work item: 1, 2 or 4, no more than a page
-  int tl = launch_tuning().compress_tile_log2 >= 0 ? launch_tuning().compress_tile_log2
-           : p.max_out_rows <= kSmallBatchRows        ? 0
-                                                      : kTileLog2;
-  tl = tl > 2 ? 2 : tl;
+  // rows per work item: the caller's 1, 2 or 4, else by batch size; no more
+  // than a page
+  int tl = p.tile_rows == 1 ? 0 : p.tile_rows == 2 ? 1 : p.tile_rows == 4 ? 2
+           : p.max_out_rows <= kSmallBatchRows ? 0 : kTileLog2;
   p.tile_log2 = tl < p.cache.page_bits ? tl : p.cache.page_bits;
   switch (p.cache.layout) {
     case kV41: return launch_layout<kV41>(p, stream);

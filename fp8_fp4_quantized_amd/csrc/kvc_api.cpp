@@ -99,30 +99,13 @@ struct kvc_kvbuf {
 
 extern "C" {
 
-int kvc_version(void) { return 2; }
+int kvc_version(void) { return 3; }
 
 const char* kvc_last_error(void) { return g_last_error.c_str(); }
 
 int kvc_layout_query(int32_t layout, kvc_layout_info* info) {
   if (info == nullptr) return fail(KVC_EINVAL, "kvc_layout_query: info is NULL");
   if (!layout_info(layout, info)) return fail(KVC_EUNSUPPORTED, "kvc_layout_query: unknown layout %d", layout);
-  return ok();
-}
-
-int kvc_set_launch_shape(int32_t gather_blocks, int32_t compress_blocks,
-                         int32_t compress_tile_rows) {
-  if (gather_blocks < 0 || compress_blocks < 0 || compress_tile_rows < 0 ||
-      compress_tile_rows > 4 || (compress_tile_rows & (compress_tile_rows - 1)) != 0)
-    return fail(KVC_EINVAL, "kvc_set_launch_shape: negative block count, or tile rows not 1, 2 "
-                            "or 4");
-  kvc::launch_tuning().gather_blocks = gather_blocks;
-  kvc::launch_tuning().compress_blocks = compress_blocks;
-  int tl = -1;
-  if (compress_tile_rows > 0) {
-    tl = 0;
-    while ((1 << tl) < compress_tile_rows) ++tl;
-  }
-  kvc::launch_tuning().compress_tile_log2 = tl;
   return ok();
 }
 
@@ -173,7 +156,7 @@ int kvc_store_rows_rope(const kvc_cache* cache, const void* rows_bf16, int64_t r
 
 int kvc_dcp_filter_ids(const int32_t* ids, int64_t T, int32_t k, int64_t ids_stride,
                        const int32_t* token_to_req, int32_t n_req, const int32_t* block_table,
-                       int64_t bt_stride, const int32_t* valid, int32_t page_size,
+                       int64_t bt_stride, int64_t bt_width, const int32_t* valid, int32_t page_size,
                        int64_t num_pages, int32_t world, int32_t rank, int32_t interleave,
                        int32_t* out_slots, int64_t out_stride, int32_t* out_lens,
                        int32_t* status, void* stream) {
@@ -194,8 +177,9 @@ int kvc_dcp_filter_ids(const int32_t* ids, int64_t T, int32_t k, int64_t ids_str
     return fail(KVC_EINVAL, "%s: NULL ids or out_slots, or a row stride below k", who);
   if (k > 0 && ((uintptr_t)out_slots & 3u) != 0)
     return fail(KVC_EINVAL, "%s: out_slots is not 4-byte aligned", who);
-  if (n_req < 0 || (n_req > 0 && (block_table == nullptr || bt_stride < 1)))
-    return fail(KVC_EINVAL, "%s: n_req < 0, or no block table", who);
+  if (n_req < 0 || (n_req > 0 && (block_table == nullptr || bt_width < 1 || bt_stride < bt_width)))
+    return fail(KVC_EINVAL, "%s: n_req < 0, or no block table, or not 1 <= bt_width <= bt_stride",
+                who);
   if (num_pages < 1 || num_pages > ((int64_t)1 << 31) / page_size)
     return fail(KVC_EINVAL, "%s: num_pages must be >= 1 with num_pages * page_size in int32", who);
   kvc::DcpFilterParams p{};
@@ -207,6 +191,7 @@ int kvc_dcp_filter_ids(const int32_t* ids, int64_t T, int32_t k, int64_t ids_str
   p.n_req = n_req;
   p.block_table = block_table;
   p.bt_stride = bt_stride;
+  p.bt_width = bt_width;
   p.valid = valid;
   p.page_bits = page_bits_of(page_size);
   p.num_pages = num_pages;
@@ -271,6 +256,8 @@ int kvc_compress_store(const kvc_compress_args* a, void* stream) {
     return fail(KVC_EINVAL, "%s: dcp_interleave %d must be >= 1 and divide page_size %d", who,
                 a->dcp_interleave, a->cache.page_size);
   if (a->num_slots < 0) return fail(KVC_EINVAL, "%s: num_slots < 0", who);
+  if (a->tile_rows != 0 && a->tile_rows != 1 && a->tile_rows != 2 && a->tile_rows != 4)
+    return fail(KVC_EINVAL, "%s: tile_rows %d (0, 1, 2 or 4)", who, a->tile_rows);
   if (a->num_slots == 0) return ok();
   if (a->mode == KVC_MODE_VERIFY && (int64_t)a->num_slots * a->draft_len > 0x7FFFFFFF)
     return fail(KVC_EINVAL, "%s: num_slots * draft_len must be below 2^31 (token indices are int32)",
@@ -279,6 +266,15 @@ int kvc_compress_store(const kvc_compress_args* a, void* stream) {
     return fail(KVC_EINVAL, "%s: prefill num_slots %d > %d", who, a->num_slots, kvc::max_prefill_slots());
   if (a->kv == nullptr || !aligned16(a->kv) || !row_stride_ok(a->kv_stride))
     return fail(KVC_EINVAL, "%s: kv must be non-NULL, 16-byte aligned, kv_stride >= 512 and a multiple of 8", who);
+  {
+    // decode / verify read token rows 0 .. num_slots * D - 1; prefill checks
+    // each slot's rows against kv_rows on the device
+    const int64_t need = a->mode == KVC_MODE_PREFILL ? 1
+                       : (int64_t)a->num_slots * (a->mode == KVC_MODE_VERIFY ? a->draft_len : 1);
+    if (a->kv_rows < need)
+      return fail(KVC_EINVAL, "%s: kv_rows %lld, need at least %lld", who, (long long)a->kv_rows,
+                  (long long)need);
+  }
   if (a->ratio == 2) {
     if (a->score == nullptr || !aligned16(a->score) || a->score_stride < 512 || a->score_stride % 8)
       return fail(KVC_EINVAL, "%s: ratio 2 needs an aligned score buffer with score_stride >= 512, a multiple of 8", who);
@@ -288,11 +284,14 @@ int kvc_compress_store(const kvc_compress_args* a, void* stream) {
   if (a->start_pos == nullptr) return fail(KVC_EINVAL, "%s: start_pos is NULL", who);
   if (a->mode == KVC_MODE_PREFILL) {
     if (a->offsets == nullptr) return fail(KVC_EINVAL, "%s: prefill needs offsets", who);
-    if (a->page_table == nullptr || a->pt_stride < 1)
-      return fail(KVC_EINVAL, "%s: prefill needs a page table with pt_stride >= 1", who);
-  } else if (a->out_loc == nullptr && (a->page_table == nullptr || a->pt_stride < 1)) {
+    if (a->page_table == nullptr)
+      return fail(KVC_EINVAL, "%s: prefill needs a page table", who);
+  } else if (a->out_loc == nullptr && a->page_table == nullptr) {
     return fail(KVC_EINVAL, "%s: decode and verify need out_loc or a page table", who);
   }
+  if (a->page_table != nullptr && (a->pt_width < 1 || a->pt_stride < a->pt_width))
+    return fail(KVC_EINVAL, "%s: page table needs 1 <= pt_width <= pt_stride (%lld, %lld)", who,
+                (long long)a->pt_width, (long long)a->pt_stride);
   if (a->norm_w == nullptr || !aligned16(a->norm_w)) return fail(KVC_EINVAL, "%s: norm_w NULL or misaligned", who);
   if (a->freqs == nullptr || !aligned16(a->freqs) || a->max_pos < 1)
     return fail(KVC_EINVAL, "%s: freqs must be non-NULL, 16-byte aligned, max_pos >= 1", who);
@@ -308,11 +307,13 @@ int kvc_compress_store(const kvc_compress_args* a, void* stream) {
   p.kv_stride = a->kv_stride;
   p.score = static_cast<const uint16_t*>(a->score);
   p.score_stride = a->score_stride;
+  p.kv_rows = a->kv_rows;
   p.num_slots = a->num_slots;
   p.offsets = a->offsets;
   p.start_pos = a->start_pos;
   p.page_table = a->page_table;
   p.pt_stride = a->page_table ? a->pt_stride : 0;
+  p.pt_width = a->page_table ? a->pt_width : 0;
   p.out_loc = a->mode != KVC_MODE_PREFILL ? a->out_loc : nullptr;
   p.state = static_cast<uint16_t*>(a->state);
   p.norm_w = static_cast<const uint16_t*>(a->norm_w);
@@ -331,6 +332,7 @@ int kvc_compress_store(const kvc_compress_args* a, void* stream) {
   p.dcp_div = kvc::div_magic((uint32_t)world);
   p.dcp_rank = world > 1 ? a->dcp_rank : 0;
   p.dcp_interleave_log2 = world > 1 ? page_bits_of(a->dcp_interleave) : 0;
+  p.tile_rows = a->tile_rows;
   return launched(kvc::launch_compress(p, static_cast<hipStream_t>(stream)), who);
 }
 

@@ -54,7 +54,8 @@ struct DcpFilterParams {
   const int32_t* token_to_req;
   int32_t n_req;
   const int32_t* block_table;
-  int64_t bt_stride;
+  int64_t bt_stride;           // entries between block-table rows
+  int64_t bt_width;            // valid entries per row (the bound)
   const int32_t* valid;        // nullable
   int32_t page_bits;
   int64_t num_pages;
@@ -89,11 +90,13 @@ struct CompressParams {
   int64_t kv_stride;
   const uint16_t* score;
   int64_t score_stride;
+  int64_t kv_rows;             // token rows kv and score hold
   int32_t num_slots;
   const int32_t* offsets;
   const int32_t* start_pos;
   const int32_t* page_table;
-  int64_t pt_stride;
+  int64_t pt_stride;           // entries between page-table rows
+  int64_t pt_width;            // valid entries per row (the bound)
   const int32_t* out_loc;
   uint16_t* state;
   const uint16_t* norm_w;
@@ -112,6 +115,7 @@ struct CompressParams {
   DivMagic dcp_div;            // division by dcp_world
   int32_t dcp_rank;
   int32_t dcp_interleave_log2; // log2 of the rows per rank turn
+  int32_t tile_rows;           // prefill rows per work item: 1, 2, 4 (0: by batch size)
   int32_t tile_log2;           // set by the launcher: log2 of rows per prefill work item
 };
 
@@ -124,13 +128,5 @@ hipError_t launch_dcp_filter(const DcpFilterParams& p, hipStream_t stream);
 
 // largest num_slots a prefill compress accepts (its LDS tables)
 int max_prefill_slots();
-
-// launch-shape overrides for tuning sweeps (0 = default)
-struct LaunchTuning {
-  int gather_blocks;           // workgroups of the gather grid
-  int compress_blocks;         // workgroups of the prefill compress grid
-  int compress_tile_log2;      // log2 of compressed rows per prefill work item (-1: default)
-};
-LaunchTuning& launch_tuning();
 
 }  // namespace kvc

@@ -81,6 +81,7 @@ enum : int32_t {
   kStLatentRange = 8,
   kStPosRange = 16,
   kStReqRange = 32,
+  kStTokenRange = 64,
 };
 
 }  // namespace kvc

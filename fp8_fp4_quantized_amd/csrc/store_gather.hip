@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kBlock) void dcp_filter_kernel(DcpFilterParams p) {
   // the page index of a kept id is below 2^(31 - pb); a row index of -1
   // (not kept) shifts to 2^(32 - pb) - 1, at or past this bound
   const uint32_t lim = 1u << (31 - pb);
-  const uint32_t bts = p.bt_stride < (int64_t)lim ? (uint32_t)p.bt_stride : lim;
+  const uint32_t bts = p.bt_width < (int64_t)lim ? (uint32_t)p.bt_width : lim;
   const uint32_t npg = (uint32_t)(p.num_pages < 0x7FFFFFFF ? p.num_pages : 0x7FFFFFFF);
   const int32_t k = p.k;
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
@@ -348,11 +348,6 @@ int grid_for(int64_t units, int64_t per_block, int cap) {
 
 }  // namespace
 
-LaunchTuning& launch_tuning() {
-  static LaunchTuning t{0, 0, -1};
-  return t;
-}
-
 hipError_t launch_store_rows(const StoreParams& p, hipStream_t stream) {
   const int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * kStoreRows, 8192);
   const bool rope = p.positions != nullptr;
@@ -382,8 +377,7 @@ hipError_t launch_dequant_gather(const GatherParams& p_in, hipStream_t stream) {
   GatherParams p = p_in;
   p.batch = kGatherBatch;
   while (p.batch > kGatherMinBatch && p.n < (int64_t)p.batch * 4096) p.batch >>= 1;
-  int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * p.batch, 8192);
-  if (launch_tuning().gather_blocks > 0) blocks = launch_tuning().gather_blocks;
+  const int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * p.batch, 8192);
   switch (p.cache.layout) {
     case kV41: return launch(dequant_gather_kernel<kV41>, blocks, p, stream);
     case kV41Fp4: return launch(dequant_gather_kernel<kV41Fp4>, blocks, p, stream);

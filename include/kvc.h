@@ -71,7 +71,8 @@ enum {
   KVC_STATUS_PT_RANGE = 4,     /* compressed row beyond its slot's page-table row          */
   KVC_STATUS_LATENT_RANGE = 8, /* latent row index >= max_out_rows                         */
   KVC_STATUS_POS_RANGE = 16,   /* rotary position < 0 or >= max_pos: row skipped           */
-  KVC_STATUS_REQ_RANGE = 32    /* request index outside the block table: row dropped        */
+  KVC_STATUS_REQ_RANGE = 32,   /* request index outside the block table: row dropped        */
+  KVC_STATUS_TOKEN_RANGE = 64  /* prefill slot's token rows outside [0, kv_rows): slot skipped */
 };
 
 /* ---------------------------------------------------------------- layouts
@@ -175,6 +176,10 @@ int kvc_store_rows_rope(const kvc_cache* cache, const void* rows_bf16, int64_t r
  *             token count (<= 0: the slot has no tokens)
  *   start_pos device int32 [num_slots]: position of slot b's first token
  *             (< 0: the slot is skipped)
+ *   kv_rows   token rows the kv (and score) buffers hold: a slot whose rows
+ *             offsets[b] .. offsets[b] + count - 1 do not lie in [0, kv_rows)
+ *             is skipped whole (no rows, no pending-state write) with
+ *             KVC_STATUS_TOKEN_RANGE
  *   Ratio 1: every token at position q gives compressed row c = q.
  *   Ratio 2: every token at an odd position q closes the pair (q - 1, q) and
  *   gives row c = q / 2; the pair's first token is the previous token, or
@@ -182,21 +187,23 @@ int kvc_store_rows_rope(const kvc_cache* cache, const void* rows_bf16, int64_t r
  *   at an even position is written to the pending state (after it is read).
  *   The rotary position of a row is p = c for ratio 1 and p = 2c (the pair's
  *   first position) for ratio 2.  out_loc = page_table[b][c / page_size] *
- *   page_size + c % page_size.  Latent rows are numbered consecutively over
- *   the batch in slot order.
+ *   page_size + c % page_size; a logical page c / page_size >= pt_width sets
+ *   KVC_STATUS_PT_RANGE and the row is not stored.  Latent rows are numbered
+ *   consecutively over the batch in slot order.
  * DECODE mode (one new token per slot):
  *   slot b's token is row b of the projection buffer at position
- *   start_pos[b] (< 0: skipped).  Ratio 1: row c = pos.  Ratio 2: an odd
- *   position pools the pending state with the token into row c = pos / 2
- *   (rotary position pos - 1); an even position writes the token to the
- *   pending state and emits no row.  out_loc = out_loc[b] when out_loc is
- *   given (0 = no cache write, a padded row), otherwise from the page table
- *   as in prefill.  The latent row of slot b is b (written only when a row is
- *   emitted).
+ *   start_pos[b] (< 0: skipped); kv_rows >= num_slots.  Ratio 1: row c =
+ *   pos.  Ratio 2: an odd position pools the pending state with the token
+ *   into row c = pos / 2 (rotary position pos - 1); an even position writes
+ *   the token to the pending state and emits no row.  out_loc = out_loc[b]
+ *   when out_loc is given (0 = no cache write, a padded row), otherwise from
+ *   the page table as in prefill.  The latent row of slot b is b (written
+ *   only when a row is emitted).
  * VERIFY mode (speculative decoding: draft_len = D tokens per slot; sglang
  *   PR #39652, Summary and Review, the decode-or-verify ratio-2 compressor):
  *   slot b's tokens are rows b*D .. b*D + D - 1 at positions start_pos[b] ..
- *   start_pos[b] + D - 1 (start_pos[b] < 0: the slot is skipped), taken in
+ *   start_pos[b] + D - 1 (start_pos[b] < 0: the slot is skipped; kv_rows >=
+ *   num_slots * D), taken in
  *   order as D decode tokens: token j's latent row and out_loc entry are
  *   b*D + j, and a ratio-2 token at an odd position pools with the previous
  *   draft token (j > 0) or with the ring entry (j = 0).  DECODE is VERIFY
@@ -239,8 +246,8 @@ typedef struct kvc_compress_args {
   const int32_t* offsets;     /* device int32 [2, S], prefill */
   const int32_t* start_pos;   /* device int32 [S] */
   const int32_t* page_table;  /* device int32 [S, pt_stride]; may be NULL only
-                                 in decode mode with out_loc */
-  int64_t pt_stride;          /* entries per page-table row */
+                                 in decode / verify mode with out_loc */
+  int64_t pt_stride;          /* entries between page-table rows (addressing) */
   const int32_t* out_loc;     /* device int32 [S * D], decode / verify only, or NULL */
   void* state;                /* device bf16 [S, ring_slots, 2, 512]: pending (kv, score), ratio 2 */
   const void* norm_w;         /* device bf16 [512] */
@@ -259,6 +266,12 @@ typedef struct kvc_compress_args {
   int32_t dcp_world;          /* decode-context-parallel ranks, 0 or 1: none; <= 1024 */
   int32_t dcp_rank;           /* 0 .. dcp_world - 1 */
   int32_t dcp_interleave;     /* consecutive rows per rank turn, >= 1, divides page_size */
+  int32_t tile_rows;          /* prefill: consecutive rows per work item, 1, 2 or 4 (0:
+                                 the library's choice, 1 for max_out_rows <= 8192, else 2);
+                                 results do not depend on it */
+  int64_t kv_rows;            /* token rows in kv and score, >= 1 */
+  int64_t pt_width;           /* valid entries per page-table row, 1 .. pt_stride (the
+                                 bound; pt_stride only addresses the rows) */
 } kvc_compress_args;
 /* Index ranges: token positions (start_pos + i) stay below 2^31, the rows a
  * prefill batch emits and the token rows of a decode / verify batch (num_slots
@@ -303,19 +316,21 @@ int kvc_dequant_gather(const kvc_cache* cache, const int32_t* page_table, int64_
  *   ids          device int32, rows of k entries, ids_stride >= k
  *   token_to_req device int32 [T]; a request outside [0, n_req) drops the
  *                row (count 0) with KVC_STATUS_REQ_RANGE
- *   block_table  device int32 [n_req, bt_stride]: this rank's pages
+ *   block_table  device int32, n_req rows of bt_width valid entries, rows
+ *                bt_stride entries apart (1 <= bt_width <= bt_stride): this
+ *                rank's pages
  *   valid        device int32 [T] or NULL; 0 = a padding token: count 0
  *   out_slots    device int32, 4-byte aligned, out_stride >= k; must not
  *                overlap ids (may be NULL when k = 0)
  *   out_lens     device int32 [T]
- * A page index >= bt_stride (KVC_STATUS_PT_RANGE) or a page < 0 or >=
+ * A page index >= bt_width (KVC_STATUS_PT_RANGE) or a page < 0 or >=
  * num_pages (KVC_STATUS_PAGE_RANGE) drops that id.  world = 1 (rank 0) maps
  * through the block table with the -1 entries squeezed out.  page_size is a
  * power of two in [1, 4096] and a multiple of interleave; 1 <= world <= 1024;
  * 0 <= k <= 65536. */
 int kvc_dcp_filter_ids(const int32_t* ids, int64_t T, int32_t k, int64_t ids_stride,
                        const int32_t* token_to_req, int32_t n_req, const int32_t* block_table,
-                       int64_t bt_stride, const int32_t* valid, int32_t page_size,
+                       int64_t bt_stride, int64_t bt_width, const int32_t* valid, int32_t page_size,
                        int64_t num_pages, int32_t world, int32_t rank, int32_t interleave,
                        int32_t* out_slots, int64_t out_stride, int32_t* out_lens,
                        int32_t* status, void* stream);
@@ -350,16 +365,8 @@ int kvc_dequant_gather_reuse(kvc_kvbuf* kb, const kvc_cache* cache, const int32_
 /* Message of the last failed call on this thread ("" if none). */
 const char* kvc_last_error(void);
 
-/* Library ABI version (this header: 2). */
+/* Library ABI version (this header: 3). */
 int kvc_version(void);
-
-/* Launch-shape knob for tuning: the number of workgroups of the gather grid,
- * the cap on the prefill compress grid and the compressed rows one prefill
- * work item takes (1, 2 or 4; 0 = the library's default for each -- for the
- * rows per item, 1 when max_out_rows <= 8192, else 2).
- * Process-wide, not thread-safe; results do not depend on it. */
-int kvc_set_launch_shape(int32_t gather_blocks, int32_t compress_blocks,
-                         int32_t compress_tile_rows);
 
 #ifdef __cplusplus
 }

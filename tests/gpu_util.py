@@ -110,11 +110,27 @@ def assert_rows_close(layout: str, gd, gs, od, os_, ref_vals):
 
 
 # --------------------------------------------------------------- compressor runs
+def _pt_view(pt, spare_cols, num_pages):
+    """device copy of page table ``pt`` [S, W]; with spare columns, a [:, :W]
+    slice of a [S, W + spare] table whose extra entries are valid pages"""
+    if not spare_cols:
+        return dev(pt)
+    S, Wd = pt.shape
+    wide = np.empty((S, Wd + spare_cols), np.int32)
+    wide[:, :Wd] = pt
+    wide[:, Wd:] = np.random.default_rng(7).integers(1, num_pages, size=(S, spare_cols))
+    return dev(wide)[:, :Wd]
+
+
 def run_compress(K, case, layout, ratio, mode, fused=True, eps=None, max_out_rows=None,
                  out_loc=None, page_table="case", want_state=True, cache_fill=0xA5,
-                 page_stride=None, **extra):
+                 page_stride=None, tile_rows=0, pt_spare_cols=0, **extra):
     """run oracle and GPU on the same inputs; returns dict of both sides.
-    ``extra``: draft_len, ring_slots and dcp_* arguments, passed to both."""
+    ``extra``: draft_len, ring_slots and dcp_* arguments, passed to both.
+    ``tile_rows`` (rows per prefill work item) goes to the GPU only.
+    ``pt_spare_cols``: the GPU's page table is a column slice of a wider
+    table whose extra columns hold valid pages (the slice's width, not its
+    row stride, must bound the lookups)."""
     ps = case["page_size"]
     db, sb, rb, _ = oracle.layout_bytes(layout)
     eps = case["eps"] if eps is None else eps
@@ -148,9 +164,10 @@ def run_compress(K, case, layout, ratio, mode, fused=True, eps=None, max_out_row
         start_pos=dev(start), cache=K.Cache(dc, layout, ps), norm_w=dev(case["norm_w"]), eps=eps,
         freqs=dev(case["freqs"]), latent_out=lat, max_out_rows=nlat,
         offsets=None if case.get("offsets") is None or mode != oracle.PREFILL else dev(case["offsets"]),
-        page_table=None if pt is None else dev(pt),
+        page_table=None if pt is None else _pt_view(pt, pt_spare_cols, case["num_pages"]),
         out_loc=None if out_loc is None else dev(out_loc),
-        state=state_d if ratio == 2 else None, prequant_out=pre, status=s, **extra)
+        state=state_d if ratio == 2 else None, prequant_out=pre, status=s, tile_rows=tile_rows,
+        **extra)
     torch.cuda.synchronize()
     return dict(lat_o=lat_o, pre_o=pre_o, st_o=st_o, n_rows=n_rows, cache_o=hc, state_o=state_h,
                 lat_g=host(lat, np.uint16)[:nlat], pre_g=host(pre, np.uint16)[:nlat],

@@ -11,8 +11,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvc.h")
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"\b(kvc_[a-z_0-9]+)\s*\(", src)
     return sorted(set(names))
@@ -33,8 +33,26 @@ def test_every_declared_symbol_is_exported(kvc):
     assert set(names) == set(kvc.SIGNATURES)
 
 
+def test_ceiling_library_exports_its_header():
+    """libkvc_ceiling.so (the benchmark's streaming yardstick) loads and
+    exports every function include/kvc_ceiling.h declares; a bad argument is
+    refused before any launch."""
+    path = os.path.join(ROOT, "fp8_fp4_quantized_amd", "libkvc_ceiling.so")
+    L = C.CDLL(path)
+    names = declared_functions(os.path.join(ROOT, "include", "kvc_ceiling.h"))
+    assert names == ["kvc_ceiling_compress_shape", "kvc_ceiling_gather_shape"]
+    for n in names:
+        assert hasattr(L, n), n
+    L.kvc_ceiling_compress_shape.argtypes = [C.c_void_p] * 4 + [C.c_int64, C.c_void_p]
+    L.kvc_ceiling_gather_shape.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]
+    assert L.kvc_ceiling_compress_shape(None, None, None, None, 0, None) == 0
+    assert L.kvc_ceiling_compress_shape(None, FAKE, FAKE, FAKE, 4, None) == -1
+    assert L.kvc_ceiling_compress_shape(FAKE, FAKE, FAKE, FAKE, -1, None) == -1
+    assert L.kvc_ceiling_gather_shape(FAKE, None, 4, None) == -1
+
+
 def test_version_and_layouts(kvc):
-    assert kvc.kvc_version() == 2
+    assert kvc.kvc_version() == 3
     want = {"V4": (576, 8, 584, 64, 448), "V41": (512, 16, 528, 32, 512),
             "V41_FP4": (256, 32, 288, 16, 512)}
     for name, w in want.items():
@@ -112,12 +130,12 @@ def test_store_and_gather_argument_checks(kvc):
 def test_dcp_filter_argument_checks(kvc):
     L = kvc.lib()
 
-    def call(T=4, k=8, ids_stride=8, t2r=FAKE, n_req=2, bt=FAKE, bt_stride=4, valid=None,
-             page_size=64, num_pages=10, world=2, rank=1, inter=4, out=FAKE, out_stride=8,
-             lens=FAKE):
-        return L.kvc_dcp_filter_ids(FAKE, T, k, ids_stride, t2r, n_req, bt, bt_stride, valid,
-                                    page_size, num_pages, world, rank, inter, out, out_stride,
-                                    lens, None, None)
+    def call(T=4, k=8, ids_stride=8, t2r=FAKE, n_req=2, bt=FAKE, bt_stride=4, bt_width=4,
+             valid=None, page_size=64, num_pages=10, world=2, rank=1, inter=4, out=FAKE,
+             out_stride=8, lens=FAKE):
+        return L.kvc_dcp_filter_ids(FAKE, T, k, ids_stride, t2r, n_req, bt, bt_stride, bt_width,
+                                    valid, page_size, num_pages, world, rank, inter, out,
+                                    out_stride, lens, None, None)
 
     assert call(T=0) == kvc.KVC_OK
     for kw in (dict(T=-1), dict(k=-1), dict(k=65537, ids_stride=65537, out_stride=65537),
@@ -125,6 +143,7 @@ def test_dcp_filter_argument_checks(kvc):
                dict(rank=2), dict(rank=-1), dict(inter=0), dict(inter=3), dict(inter=128),
                dict(t2r=None), dict(out=None), dict(lens=None), dict(ids_stride=7),
                dict(out_stride=4), dict(n_req=-1), dict(bt=None), dict(bt_stride=0),
+               dict(bt_width=0), dict(bt_width=5),
                dict(num_pages=0), dict(num_pages=1 << 30), dict(out=FAKE + 2)):
         assert call(**kw) == kvc.KVC_EINVAL, kw
         assert kvc.kvc_last_error()
@@ -135,7 +154,8 @@ def _args(kvc, **kw):
     a.ratio, a.mode = 2, kvc.MODE_PREFILL
     a.kv, a.kv_stride, a.score, a.score_stride = FAKE, 1024, FAKE + 1024, 1024
     a.num_slots = 4
-    a.offsets, a.start_pos, a.page_table, a.pt_stride = FAKE, FAKE, FAKE, 8
+    a.offsets, a.start_pos, a.page_table, a.pt_stride, a.pt_width = FAKE, FAKE, FAKE, 8, 8
+    a.kv_rows = 64
     a.state, a.norm_w, a.eps, a.freqs, a.max_pos = FAKE, FAKE, 1e-6, FAKE, 100
     a.latent_out, a.latent_stride, a.max_out_rows = FAKE, 512, 10
     a.cache = _cache(kvc, layout=2, page_size=128)
@@ -149,9 +169,14 @@ def test_compress_argument_checks(kvc):
     bad_inval = [
         dict(kv=0), dict(kv_stride=500), dict(kv=FAKE + 4), dict(score=0), dict(score_stride=4),
         dict(state=0), dict(offsets=0), dict(start_pos=0), dict(page_table=0),
-        dict(pt_stride=0), dict(norm_w=0), dict(freqs=0), dict(max_pos=0), dict(latent_out=0),
+        dict(pt_stride=0), dict(pt_width=0), dict(pt_width=9), dict(norm_w=0), dict(freqs=0),
+        dict(max_pos=0), dict(latent_out=0),
         dict(latent_stride=256), dict(max_out_rows=-1), dict(num_slots=-1),
         dict(num_slots=8192), dict(eps=-1.0), dict(prequant_out=FAKE, prequant_stride=3),
+        dict(kv_rows=0), dict(tile_rows=3), dict(tile_rows=8), dict(tile_rows=-1),
+        # decode / verify read token rows 0 .. num_slots * D - 1
+        dict(mode=kvc.MODE_DECODE, kv_rows=3),
+        dict(mode=kvc.MODE_VERIFY, draft_len=4, kv_rows=15),
     ]
     for kw in bad_inval:
         a = _args(kvc, **kw)
@@ -242,4 +267,80 @@ def test_binding_rejects_host_and_mistyped_tensors(kvc):
     with pytest.raises(ValueError, match="kv"):
         kvc.kvc_compress_store(ratio=1, mode=kvc.MODE_PREFILL, kv=out, score=None,
                                start_pos=ids, cache=cache, norm_w=out[0], eps=1e-6,
-                               freqs=torch.zeros((4, 64)), latent_out=out)
+                               freqs=torch.zeros((4, 64)), latent_out=out,
+                               offsets=torch.zeros((2, 4), dtype=torch.int32),
+                               page_table=torch.zeros((4, 2), dtype=torch.int32))
+
+
+def test_binding_checks_sizes_against_counts(kvc):
+    """Every count the binding hands the library (rows, ids, slots, tokens,
+    table rows, output capacity) is checked against the tensors' shapes on
+    the host before any launch: a mismatch that would let a kernel read or
+    write past an allocation raises ValueError.  Host tensors reach these
+    checks first, so no GPU is needed."""
+    import torch
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)
+    b16 = lambda *s: torch.zeros(s, dtype=torch.int16)
+    cache = kvc.Cache(torch.zeros((4, 64 * 528), dtype=torch.uint8), "V41", 64)
+    # gather: output rows against ids
+    with pytest.raises(ValueError, match="out: 3 rows for 4 ids"):
+        kvc.kvc_dequant_gather(cache, None, i32(4), b16(3, 512))
+    with pytest.raises(ValueError, match="columns"):
+        kvc.kvc_dequant_gather(cache, None, i32(4), b16(4, 256))
+    buf = kvc.KVBuf()
+    with pytest.raises(ValueError, match="out: 3 rows"):
+        buf.kvc_dequant_gather_reuse(cache, None, i32(4), b16(3, 512))
+    # stores: out_loc and positions against rows, the rotary table's width
+    with pytest.raises(ValueError, match="out_loc: 2 entries for 3 rows"):
+        kvc.kvc_store_rows(cache, b16(3, 512), i32(2))
+    with pytest.raises(ValueError, match="positions"):
+        kvc.kvc_store_rows_rope(cache, b16(3, 512), i32(2), torch.zeros((8, 64)), i32(3))
+    with pytest.raises(ValueError, match="freqs"):
+        kvc.kvc_store_rows_rope(cache, b16(3, 512), i32(3), torch.zeros((8, 32)), i32(3))
+    # DCP filter: outputs and per-row inputs against [T, k]
+    ids = i32(5, 8)
+    good = dict(token_to_req=i32(5), block_table=i32(2, 4), out_slots=i32(5, 8),
+                out_lens=i32(5), page_size=64, num_pages=10, world=2, rank=0, interleave=4)
+    for key, bad in (("out_slots", i32(5, 7)), ("out_slots", i32(4, 8)), ("out_lens", i32(4)),
+                     ("token_to_req", i32(4)), ("valid", i32(4)), ("block_table", i32(8))):
+        kw = dict(good, **{key: bad})
+        with pytest.raises(ValueError, match=key):
+            kvc.kvc_dcp_filter_ids(ids, **kw)
+
+    # compressor
+    S = 4
+
+    def comp(**kw):
+        base = dict(ratio=2, mode=kvc.MODE_PREFILL, kv=b16(64, 1024)[:, :512],
+                    score=b16(64, 1024)[:, 512:], start_pos=i32(S), cache=cache,
+                    norm_w=b16(512), eps=1e-6, freqs=torch.zeros((64, 64)),
+                    latent_out=b16(16, 512), offsets=i32(2, S), page_table=i32(S, 2),
+                    state=b16(S, 2, 512))
+        base.update(kw)
+        kvc.kvc_compress_store(**base)
+
+    cases = [
+        (dict(max_out_rows=17), "max_out_rows 17"),              # past latent_out
+        (dict(prequant_out=b16(8, 512)), "prequant_out"),          # fewer rows than max_out_rows
+        (dict(prequant_out=b16(16, 512), max_out_rows=20), "max_out_rows 20"),
+        (dict(state=b16(S, 2, 256)), "state"),                     # too small a ring
+        (dict(state=b16(S, 2, 512), ring_slots=2), "state"),
+        (dict(offsets=i32(2, S - 1)), "offsets"),
+        (dict(offsets=None), "offsets"),
+        (dict(page_table=i32(S - 1, 2)), "page_table"),
+        (dict(page_table=i32(S * 2)), "page_table"),
+        (dict(norm_w=b16(256)), "norm_w"),
+        (dict(freqs=torch.zeros((64, 32))), "freqs"),
+        (dict(kv=b16(64, 256)), "kv"),
+        (dict(latent_out=b16(16, 128)), "latent_out"),
+        # decode / verify: token rows, out_loc entries and latent rows per token
+        (dict(mode=kvc.MODE_VERIFY, draft_len=4, latent_out=b16(15, 512), offsets=None,
+              kv=b16(16, 512), score=b16(16, 512)), "max_out_rows"),
+        (dict(mode=kvc.MODE_VERIFY, draft_len=4, latent_out=b16(16, 512), offsets=None,
+              kv=b16(15, 512), score=b16(16, 512)), "kv: 15 token rows"),
+        (dict(mode=kvc.MODE_DECODE, offsets=None, kv=b16(4, 512), score=b16(4, 512),
+              out_loc=i32(3)), "out_loc"),
+    ]
+    for kw, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            comp(**kw)

@@ -272,3 +272,90 @@ def test_dcp_filter_widest_row(K):
             torch.cuda.synchronize()
             assert np.array_equal(host(lens), want[1]) and np.array_equal(host(out), want[0])
             assert int(s.item()) == want[2]
+
+
+@pytest.mark.parametrize("ratio", [1, 2])
+def test_prefill_page_table_slice(K, ratio):
+    """The page table passed as a column slice pt[:, :W] of a wider table
+    whose spare columns hold valid pages: a row whose logical page is at or
+    past W raises KVC_STATUS_PT_RANGE and is not stored (the width bounds the
+    lookup; the row stride only addresses the rows), as the oracle does with
+    the W-column table."""
+    _say("prefill page-table slice", ratio)
+    ps, Wd = 8, 3
+    lengths, P = [70, 0, 33, 130], [0, 0, 5, 2]
+    case = W.compress_case(470 + ratio, lengths, start_pos=P, ratio=ratio, page_size=ps,
+                           fused=True)
+    narrow = np.ascontiguousarray(case["page_table"][:, :Wd])
+    r = run_compress(K, case, "V41", ratio, oracle.PREFILL, page_table=narrow, pt_spare_cols=4)
+    assert r["st_o"] & oracle.ST_PT_RANGE
+    lat, slots, L = [], [], 0
+    for b in range(len(lengths)):
+        n, p0 = lengths[b], P[b]
+        qs = range(p0, p0 + n) if ratio == 1 else [q for q in range(p0, p0 + n) if q % 2 == 1]
+        for q in qs:
+            c = q if ratio == 1 else q // 2
+            slots.append(int(narrow[b, c // ps]) * ps + c % ps if c // ps < Wd else 0)
+            lat.append(L)
+            L += 1
+    assert 0 in slots and any(s != 0 for s in slots)
+    check_compress(r, "V41", ps, slots, lat)
+
+
+@pytest.mark.parametrize("ratio", [1, 2])
+def test_prefill_token_rows_outside_buffer(K, ratio):
+    """A slot whose extend rows run past the projection buffer, and one that
+    starts before it, are skipped whole (no rows, no pending-state write)
+    with KVC_STATUS_TOKEN_RANGE; the other slots are unaffected."""
+    _say("prefill token rows outside the buffer", ratio)
+    lengths, P = [40, 25, 31, 9], [0, 3, 1, 4]
+    case = W.compress_case(480 + ratio, lengths, start_pos=P, ratio=ratio, page_size=16,
+                           fused=True)
+    T = case["kv"].shape[0]
+    off = case["offsets"].copy()
+    off[0, 1] = T - 10          # rows T-10 .. T+14
+    off[0, 2] = -2              # rows -2 .. 28
+    case = dict(case, offsets=off)
+    r = run_compress(K, case, "V41_FP4", ratio, oracle.PREFILL)
+    assert r["st_o"] == oracle.ST_TOKEN_RANGE
+    lat, slots, L = [], [], 0
+    for b in (0, 3):
+        n, p0 = lengths[b], P[b]
+        qs = range(p0, p0 + n) if ratio == 1 else [q for q in range(p0, p0 + n) if q % 2 == 1]
+        for q in qs:
+            c = q if ratio == 1 else q // 2
+            slots.append(int(case["page_table"][b, c // 16]) * 16 + c % 16)
+            lat.append(L)
+            L += 1
+    assert r["n_rows"] == L
+    check_compress(r, "V41_FP4", 16, slots, lat)
+
+
+def test_dcp_filter_block_table_slice(K):
+    """The block table passed as a column slice bt[:, :W] of a wider table
+    whose spare columns hold valid pages: ids whose page is at or past W are
+    dropped with KVC_STATUS_PT_RANGE, as the oracle does with the W-column
+    table."""
+    _say("dcp filter block-table slice")
+    c = W.dcp_ids_case(490, T=64, k=700, n_req=4, max_rows=6000, world=2, page_size=64)
+    ids = c["ids"]
+    for rank in range(2):
+        bt = c["block_tables"][rank]
+        Wd = 8                  # ids of requests past 1024 rows reach page 8
+        narrow = np.ascontiguousarray(bt[:, :Wd])
+        want = oracle.dcp_filter_ids(ids, c["token_to_req"], narrow, page_size=64,
+                                     num_pages=c["num_pages"], world=2, rank=rank, interleave=4,
+                                     valid=c["valid"])
+        assert want[2] & oracle.ST_PT_RANGE
+        wide = np.concatenate([narrow, np.random.default_rng(491).integers(
+            0, c["num_pages"], size=(bt.shape[0], 5)).astype(np.int32)], axis=1)
+        T, k = ids.shape
+        out = torch.full((T, k), 12345, dtype=torch.int32, device="cuda")
+        lens = torch.full((T,), -7, dtype=torch.int32, device="cuda")
+        s = torch.zeros(1, dtype=torch.int32, device="cuda")
+        K.kvc_dcp_filter_ids(dev(ids), dev(c["token_to_req"]), dev(wide)[:, :Wd], out, lens,
+                             page_size=64, num_pages=c["num_pages"], world=2, rank=rank,
+                             interleave=4, valid=dev(c["valid"]), status=s)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(lens), want[1]) and np.array_equal(host(out), want[0])
+        assert int(s.item()) == want[2]

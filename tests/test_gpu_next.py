@@ -609,11 +609,7 @@ def test_prefill_every_tile_shape(K, tile_rows, layout, ratio, slots):
     P = rng.integers(0, 120, size=slots)
     case = W.compress_case(310 + tile_rows, lengths, start_pos=P, ratio=ratio, page_size=8,
                            fused=True, gap=2)
-    K.kvc_set_launch_shape(0, 0, tile_rows)
-    try:
-        r = run_compress(K, case, layout, ratio, oracle.PREFILL)
-    finally:
-        K.kvc_set_launch_shape(0, 0, 0)
+    r = run_compress(K, case, layout, ratio, oracle.PREFILL, tile_rows=tile_rows)
     lat, slots_ = [], []
     L = 0
     for b in range(len(lengths)):
