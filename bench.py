@@ -9,9 +9,22 @@ One step = one pass of both halves of the path over one batch:
 Inputs are seeded synthetic data, resident in HBM before timing starts.
 
 Prints one JSON line.  ``value`` is compressed KV rows per second over the
-step (rows compressed + rows gathered); the per-kernel HBM rates, the roofline
-object of the dominant kernel (the gather) and the CPU-oracle baseline ride
-along.
+timed steps (rows compressed + rows gathered).  Each headline kernel is also
+timed launch by launch (median and p90 over --launches calls) under three
+cache conditions:
+  steady      back to back, every call on other buffers than the calls
+              before it (no reuse of what they left in the 256 MB Infinity
+              Cache), as in a pipeline that keeps the device busy;
+  cold        before each call a 512 MB scratch write and then a 512 MB
+              scratch read, neither timed: the caches hold nothing of the
+              call's data, and the write's dirty lines have reached HBM;
+  cold_dirty  before each call the 512 MB scratch write alone (the flush as
+              first specified): the call's interval then also carries the
+              write-back of those dirty lines.
+Beside each kernel, a streaming kernel that moves the same bytes with no
+work (libkvc_ceiling.so) is timed the same way, and a 1 GiB device copy
+gives the copy ceiling.  The roofline object is the gather's (the dominant
+kernel), steady.  The CPU oracle is timed on the host's cores.
 """
 from __future__ import annotations
 
@@ -28,6 +41,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+FLUSH_BYTES = 512 << 20        # exceeds the 256 MB Infinity Cache plus the L2s
 
 
 def log(*a):
@@ -50,6 +64,105 @@ def measured_traffic(kernel: str):
     if h.hexdigest()[:16] != e.get("source_hash"):
         return None
     return e.get("bytes_per_launch")
+
+
+TRAFFIC_SOURCE = ("profiles/traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE per dispatch, "
+                  "scaled by the same counters on a 1 GiB copy; not measured in this run; "
+                  "null once the kernel's sources differ from the counted build")
+
+
+class Timer:
+    """Device time per launch of a kernel under three cache conditions, from
+    HIP events on the launch stream (calls[k % len] is launch k):
+      steady      a HIP graph of 10 back-to-back launches, replayed after an
+                  untimed lead-in replay; one sample per replay (its mean per
+                  launch), so no host launch cost falls inside an interval;
+      cold        lone launches, each after a 512 MB scratch write and a
+                  512 MB scratch read (neither timed), each bracketed by
+                  events: the caches hold none of the call's data and no
+                  dirty line; the interval carries the launch's dispatch and
+                  completion (about 3 us at these sizes, the same for the
+                  streaming yardstick timed beside it);
+      cold_dirty  the same after the scratch write alone: the interval also
+                  carries the write-back of the scratch's dirty lines."""
+
+    PER_GRAPH = 10
+
+    def __init__(self, dev, launches: int):
+        import torch
+        self.torch = torch
+        self.scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.launches = launches
+
+    def write_flush(self):
+        self.scratch.fill_(1)
+
+    def read_flush(self):
+        self.torch.amax(self.scratch.view(self.torch.int64))
+
+    def steady(self, calls):
+        torch = self.torch
+        n = self.PER_GRAPH
+        body = lambda: [calls[k % len(calls)]() for k in range(n)]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            body()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        samples = []
+        for _ in range(max(1, self.launches // n)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g.replay()                       # untimed lead-in: the device is busy
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            samples.append(a.elapsed_time(b) * 1e3 / n)
+        return samples
+
+    def flushed(self, calls, dirty: bool):
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        pairs = []
+        for k in range(self.launches):
+            self.write_flush()
+            if not dirty:
+                self.read_flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            calls[k % len(calls)]()
+            b.record(stream)
+            pairs.append((a, b))
+            if len(pairs) % 25 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in pairs]
+
+    def all(self, calls):
+        return {"steady": self.steady(calls), "cold": self.flushed(calls, dirty=False),
+                "cold_dirty": self.flushed(calls, dirty=True)}
+
+
+def summarize(samples_us, nbytes, units, unit_name, ceiling_us=None, per_sample=Timer.PER_GRAPH):
+    import numpy as np
+    med = float(np.median(samples_us))
+    r = {"us": med, "p90_us": float(np.percentile(samples_us, 90)),
+         "min_us": float(np.min(samples_us)), "samples": len(samples_us),
+         "launches_timed": len(samples_us) * per_sample,
+         "gbps": nbytes / med / 1e3, "frac": nbytes / med / 1e3 / HBM_PEAK_GBS,
+         unit_name: units / med * 1e6}
+    if ceiling_us is not None:
+        c = float(np.median(ceiling_us))
+        r["same_shape_stream_us"] = c
+        r["frac_of_same_shape_stream"] = c / med
+    return r
 
 
 def _time_events(fn, stream, reps: int, warmup: int = 3):
@@ -80,19 +193,27 @@ def _time_events(fn, stream, reps: int, warmup: int = 3):
     return a.elapsed_time(b) / (3 * reps) / 1e3
 
 
-def measure_next_rows(kvc, W, d, dev, stream):
+def measure_next_rows(kvc, W, d, dev, stream, timer):
     """Throughput of the entry points beyond the two headline kernels, each on
-    a workload of the path's own shapes, with its algorithmic HBM bytes."""
+    a workload of the path's own shapes, with its algorithmic HBM bytes.
+    These are timed as graph replays of back-to-back calls on the same
+    buffers (warm, as a decode step's freshly written inputs would be); the
+    ratio-1 store and dequant rows of the 8-request workload are also timed
+    cold (the flush before each call, median and p90)."""
     import numpy as np
     import torch
 
     res = {}
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    def entry(name, secs, nbytes, units, unit):
+    def entry(name, secs, nbytes, units, unit, cold_call=None):
         res[name] = {"us": secs * 1e6, "bytes": int(nbytes), "gbps": nbytes / secs / 1e9,
                      "frac": nbytes / secs / 1e9 / HBM_PEAK_GBS, unit: units / secs,
+                     "condition": "warm (graph replay, same buffers)",
                      "traffic": measured_traffic(name)}
+        if cold_call is not None:
+            res[name]["cold"] = summarize(timer.flushed([cold_call], dirty=False), nbytes,
+                                          units, unit, per_sample=1)
 
     # verify: 1024 slots x 4 drafts, ring of 3, V41_FP4 cache through page tables
     vc = W.verify_case(20261206, 1024, draft_len=4, ratio=2, page_size=64, max_pos=4096,
@@ -143,22 +264,24 @@ def measure_next_rows(kvc, W, d, dev, stream):
     rcache = kvc.Cache(torch.zeros((c2["num_pages"], 64 * fp4.row_bytes), dtype=torch.uint8,
                                    device=dev), "V41_FP4", 64)
     rrows, rloc = d(c2["rows"]), d(c2["out_loc"])
-    secs = _time_events(lambda: kvc.kvc_store_rows(rcache, rrows, rloc, status), stream, 50)
-    entry("store_c2_v41fp4", secs, n2 * (1024 + fp4.row_bytes + 4), n2, "rows_per_s")
+    st_fp4 = lambda: kvc.kvc_store_rows(rcache, rrows, rloc, status)
+    secs = _time_events(st_fp4, stream, 50)
+    entry("store_c2_v41fp4", secs, n2 * (1024 + fp4.row_bytes + 4), n2, "rows_per_s", st_fp4)
     # the dequant half of the same workload: every stored row back to bf16 by
     # its slot (no page table)
     dq_out = torch.empty((n2, 512), dtype=torch.int16, device=dev)
-    secs = _time_events(lambda: kvc.kvc_dequant_gather(rcache, None, rloc, dq_out, status),
-                        stream, 50)
-    entry("dequant_c2_v41fp4", secs, n2 * (fp4.row_bytes + 1024 + 4), n2, "rows_per_s")
+    dq_fp4 = lambda: kvc.kvc_dequant_gather(rcache, None, rloc, dq_out, status)
+    secs = _time_events(dq_fp4, stream, 50)
+    entry("dequant_c2_v41fp4", secs, n2 * (fp4.row_bytes + 1024 + 4), n2, "rows_per_s", dq_fp4)
     v41c = kvc.kvc_layout_query("V41")
     vcache = kvc.Cache(torch.zeros((c2["num_pages"], 64 * v41c.row_bytes), dtype=torch.uint8,
                                    device=dev), "V41", 64)
-    secs = _time_events(lambda: kvc.kvc_store_rows(vcache, rrows, rloc, status), stream, 50)
-    entry("store_c2_v41", secs, n2 * (1024 + v41c.row_bytes + 4), n2, "rows_per_s")
-    secs = _time_events(lambda: kvc.kvc_dequant_gather(vcache, None, rloc, dq_out, status),
-                        stream, 50)
-    entry("dequant_c2_v41", secs, n2 * (v41c.row_bytes + 1024 + 4), n2, "rows_per_s")
+    st_v41 = lambda: kvc.kvc_store_rows(vcache, rrows, rloc, status)
+    secs = _time_events(st_v41, stream, 50)
+    entry("store_c2_v41", secs, n2 * (1024 + v41c.row_bytes + 4), n2, "rows_per_s", st_v41)
+    dq_v41 = lambda: kvc.kvc_dequant_gather(vcache, None, rloc, dq_out, status)
+    secs = _time_events(dq_v41, stream, 50)
+    entry("dequant_c2_v41", secs, n2 * (v41c.row_bytes + 1024 + 4), n2, "rows_per_s", dq_v41)
     secs = _time_events(lambda: kvc.kvc_store_rows_rope(rcache, rrows, pos2, fr2, rloc, status),
                         stream, 50)
     entry("rope_store_c2_v41fp4", secs, n2 * (1024 + fp4.row_bytes + 8), n2, "rows_per_s")
@@ -230,12 +353,13 @@ def measure_reuse(kvc, cache, pt, idsets, outs, stream, layers: int, forwards: i
 
     def fwd_reuse(f):
         buf.begin_forward()
-        return sum(int(buf.kvc_dequant_gather_reuse(cache, pt, idsets[f % 4], outs[f % 3]))
+        return sum(int(buf.kvc_dequant_gather_reuse(cache, pt, idsets[f % len(idsets)],
+                                                    outs[f % len(outs)]))
                    for _ in range(layers))
 
     def fwd_fresh(f):
         for _ in range(layers):
-            kvc.kvc_dequant_gather(cache, pt, idsets[f % 4], outs[f % 3])
+            kvc.kvc_dequant_gather(cache, pt, idsets[f % len(idsets)], outs[f % len(outs)])
         return 0
 
     res = {"layers": layers, "forwards": forwards}
@@ -340,11 +464,61 @@ def measure_sweep(kvc, W, d, dev, stream):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(c3, c4, fp4_row_bytes):
+    """The oracle as it stands, on the host's cores, on a bounded sample of
+    each half: the compress of the first 4 requests of the 32,768-token batch
+    and the gather of the first 65,536 ids; each timed 5 times, the median
+    kept.  `value` is rows per second of the two samples run back to back."""
+    import numpy as np
+    import oracle
+    lengths = c3["lengths"].astype(np.int64)
+    n4 = int(lengths[:4].sum())
+    rows_c = int((lengths[:4] // 2).sum())
+    m = 65536
+    ids = c4["ids"][:m]
+    comp_s, gath_s = [], []
+    for _ in range(5):
+        cache_h = np.zeros((c3["num_pages"], 128 * fp4_row_bytes), np.uint8)
+        t = time.perf_counter()
+        oracle.compress(ratio=2, mode=oracle.PREFILL, kv=c3["kv"][:n4], fused=True,
+                        offsets=c3["offsets"][:, :4].copy(), start_pos=c3["start_pos"][:4],
+                        page_table=c3["page_table"][:4], state=c3["state"][:4].copy(),
+                        norm_w=c3["norm_w"], eps=c3["eps"], freqs=c3["freqs"], cache=cache_h,
+                        layout="V41_FP4", page_size=128, want_prequant=False)
+        comp_s.append(time.perf_counter() - t)
+        t = time.perf_counter()
+        oracle.dequant_gather(c4["cache"], "V41", 64, c4["page_table"], ids)
+        gath_s.append(time.perf_counter() - t)
+    tc, tg = float(np.median(comp_s)), float(np.median(gath_s))
+    return {"value": (rows_c + m) / (tc + tg), "unit": "rows/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"compress of the first 4 requests ({rows_c} rows) and gather of the "
+                      f"first {m} ids, each timed 5 times, median",
+            "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "halves": {"compress_store": {"rows": rows_c, "median_s": tc,
+                                          "rows_per_s": rows_c / tc, "runs_s": comp_s},
+                       "dequant_gather": {"rows": m, "median_s": tg, "rows_per_s": m / tg,
+                                          "runs_s": gath_s}}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--launches", type=int, default=100,
+                    help="timed launches per kernel and cache condition (median, p90)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the verify / RoPE-store / DCP-filter / graph-replay / reuse measurements")
@@ -364,6 +538,7 @@ def main() -> int:
     import torch
 
     import fp8_fp4_quantized_amd as kvc
+    from fp8_fp4_quantized_amd import ceiling
     import workloads as W
 
     dev = torch.device("cuda:0")
@@ -377,17 +552,15 @@ def main() -> int:
         print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
                           "launches": 5}), flush=True)
         return 0
-    if args.sweep:
-        def d(a):
-            a = np.ascontiguousarray(a)
-            return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
-        for rec in measure_sweep(kvc, W, d, dev, torch.cuda.current_stream()):
-            print(json.dumps(rec), flush=True)
-        return 0
 
     def d(a):
         a = np.ascontiguousarray(a)
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    if args.sweep:
+        for rec in measure_sweep(kvc, W, d, dev, torch.cuda.current_stream()):
+            print(json.dumps(rec), flush=True)
+        return 0
 
     # ---------------------------------------------------------------- inputs
     t0 = time.time()
@@ -399,46 +572,39 @@ def main() -> int:
     c3_tails = int((lengths % 2).sum())
     fp4 = kvc.kvc_layout_query("V41_FP4")
     v41 = kvc.kvc_layout_query("V41")
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    # four copies of the projection buffer (64 MB each) and three latent
-    # outputs and caches used in turn, like the gather's id lists and outputs
-    # below: back-to-back compresses read and write HBM, not lines the
-    # previous call left in the 256 MB Infinity Cache
+    # eight copies of the projection buffer (512 MB) and four latent outputs
+    # and caches, used in turn: a call reads and writes other lines than the
+    # calls just before it, so nothing it touches is left in the 256 MB
+    # Infinity Cache by them
     proj = d(c3["kv"])
-    c3_projs = [proj] + [proj.clone() for _ in range(3)]
-    c3_lats = [torch.empty((c3_rows, 512), dtype=torch.int16, device=dev) for _ in range(3)]
+    c3_projs = [proj] + [proj.clone() for _ in range(7)]
+    c3_lats = [torch.empty((c3_rows, 512), dtype=torch.int16, device=dev) for _ in range(4)]
     c3_caches = [kvc.Cache(torch.zeros((c3["num_pages"], 128 * fp4.row_bytes), dtype=torch.uint8,
-                                       device=dev), "V41_FP4", 128) for _ in range(3)]
-    c3_args = dict(
+                                       device=dev), "V41_FP4", 128) for _ in range(4)]
+    c3_common = dict(
         ratio=2, mode=kvc.MODE_PREFILL,
         start_pos=d(c3["start_pos"]), offsets=d(c3["offsets"]), page_table=d(c3["page_table"]),
-        state=d(c3["state"]), norm_w=d(c3["norm_w"]), eps=c3["eps"], freqs=d(c3["freqs"]))
+        state=d(c3["state"]), norm_w=d(c3["norm_w"]), eps=c3["eps"], freqs=d(c3["freqs"]),
+        status=status)
+    compress_calls = [kvc.prepare_compress_store(
+        **c3_common, kv=c3_projs[k % 8][:, :512], score=c3_projs[k % 8][:, 512:],
+        latent_out=c3_lats[k % 4], cache=c3_caches[k % 4]) for k in range(8)]
     g_cache = kvc.Cache(d(c4["cache"]), "V41", 64)
     g_pt = d(c4["page_table"])
     n_ids = int(c4["ids"].size)
-    # four id lists and three output buffers used in turn: a step neither
-    # reads the rows nor rewrites the lines the previous steps left in the
-    # 256 MB Infinity Cache, so the gather's reads and writes reach HBM as
-    # they would in a forward pass (cold, not cache-served)
-    g_idsets = [d(ids) for ids in W.workload_c4_id_sets(4)]
-    g_outs = [torch.empty((n_ids, 512), dtype=torch.int16, device=dev) for _ in range(3)]
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-
-    stream = torch.cuda.current_stream()
-
-    def compress(k):
-        pj = c3_projs[k % 4]
-        kvc.kvc_compress_store(**c3_args, kv=pj[:, :512], score=pj[:, 512:],
-                               latent_out=c3_lats[k % 3], cache=c3_caches[k % 3], status=status)
-
-    def gather(k):
-        kvc.kvc_dequant_gather(g_cache, g_pt, g_idsets[k % 4], g_outs[k % 3], status)
+    # four id lists that share no row and four outputs, used in turn
+    g_idsets = [d(ids) for ids in W.workload_c4_disjoint_id_sets(4)]
+    g_outs = [torch.empty((n_ids, 512), dtype=torch.int16, device=dev) for _ in range(4)]
+    gather_calls = [kvc.prepare_dequant_gather(g_cache, g_pt, g_idsets[k % 4], g_outs[k % 4],
+                                               status) for k in range(4)]
 
     def step(k):
-        compress(k)
-        gather(k)
+        compress_calls[k % 8]()
+        gather_calls[k % 4]()
 
-    # ---------------------------------------------------------------- timing
+    # ---------------------------------------------------------------- timed steps
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
@@ -451,56 +617,75 @@ def main() -> int:
     elapsed = time.perf_counter() - t_start
     ms_step = elapsed * 1e3 / args.steps
 
-    # per-kernel durations: HIP events on the launch stream around replays of
-    # HIP graphs of 10 back-to-back launches of one kernel (each with its
-    # inputs and outputs in turn).  An untimed compress replay comes
-    # first, so the device is busy when the first event is reached and no
-    # host launch latency falls inside an interval; the gathers follow the
-    # compresses, as in a step.
-    def capture(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        g.replay()
-        return g
-
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        compress(0)
-        gather(0)
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    g_comp = capture(lambda: [compress(k) for k in range(10)])
-    g_gath = capture(lambda: [gather(k) for k in range(10)])
-    torch.cuda.synchronize()
-    runs = max(args.steps // 10, 2)
-    comp_ms, gath_ms = [], []
-    for r in range(runs):
-        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        g_comp.replay()
-        a.record(stream)
-        g_comp.replay()
-        b.record(stream)
-        g_gath.replay()
-        c.record(stream)
-        torch.cuda.synchronize()
-        comp_ms.append(a.elapsed_time(b) / 10)
-        gath_ms.append(b.elapsed_time(c) / 10)
-    assert int(status.item()) == 0, f"device status {int(status.item())}"
-
+    # ---------------------------------------------------------------- per kernel
+    timer = Timer(dev, args.launches)
     comp_bytes = c3_rows * (4096 + 1024 + fp4.row_bytes) + c3_tails * 2 * 2048
     gath_bytes = n_ids * (v41.row_bytes + 1024 + 4)
-    comp_s = float(np.mean(comp_ms)) / 1e3
-    gath_s = float(np.mean(gath_ms)) / 1e3
-    comp_gbs = comp_bytes / comp_s / 1e9
-    gath_gbs = gath_bytes / gath_s / 1e9
+    t_comp = timer.all(compress_calls)
+    t_gath = timer.all(gather_calls)
+    assert int(status.item()) == 0, f"device status {int(status.item())}"
+
+    # the same bytes with no work: the compressor's shape (one item = two
+    # rows) and the gather's shape (contiguous rows), eight inputs / four
+    # outputs in turn like the kernels
+    items = (c3_rows + 1) // 2
+    cs_src = [torch.empty(items * 8192, dtype=torch.uint8, device=dev).fill_(k) for k in range(8)]
+    cs_out = [[torch.empty(items * n, dtype=torch.uint8, device=dev) for n in (2048, 512, 64)]
+              for _ in range(4)]
+    cs_calls = [ceiling.compress_shape(cs_src[k % 8], *cs_out[k % 4], items) for k in range(8)]
+    gs_src = [torch.empty(n_ids * 528, dtype=torch.uint8, device=dev).fill_(k) for k in range(4)]
+    gs_out = [torch.empty(n_ids * 1024, dtype=torch.uint8, device=dev) for _ in range(4)]
+    gs_calls = [ceiling.gather_shape(gs_src[k], gs_out[k], n_ids) for k in range(4)]
+    c_comp = timer.all(cs_calls)
+    c_gath = timer.all(gs_calls)
+    cs_bytes = items * (8192 + 2048 + 512 + 64)
+    gs_bytes = n_ids * (528 + 1024)
+    # the copy ceiling: 1 GiB device-to-device copies, two pairs in turn
+    cp = [(torch.ones(1 << 30, dtype=torch.uint8, device=dev),
+           torch.empty(1 << 30, dtype=torch.uint8, device=dev)) for _ in range(2)]
+    cp_calls = [lambda s=s_, t=t_: t.copy_(s) for s_, t_ in cp]
+    saved, timer.launches = timer.launches, 10
+    t_copy = {"steady": timer.steady(cp_calls), "cold": timer.flushed(cp_calls, dirty=False)}
+    timer.launches = saved
+    copy_gbs = {c: (2 << 30) / float(np.median(v)) / 1e3 for c, v in t_copy.items()}
+    del cs_src, cs_out, cs_calls, gs_src, gs_out, gs_calls, cp, cp_calls
+
+    def kernel_entry(t, c, nbytes, ceil_bytes, rows, traffic_name):
+        e = {"bytes": nbytes, "rows": rows,
+             "timing": "steady: HIP events around HIP-graph replays of 10 back-to-back launches, "
+                       "one sample per replay; cold, cold_dirty: lone launches after the flush, "
+                       "each bracketed by events (dispatch and completion included)"}
+        for cond in ("steady", "cold", "cold_dirty"):
+            r = summarize(t[cond], nbytes, rows, "rows_per_s",
+                          per_sample=Timer.PER_GRAPH if cond == "steady" else 1)
+            cm = float(np.median(c[cond]))
+            r["same_shape_stream_us"] = cm
+            r["same_shape_stream_frac"] = ceil_bytes / cm / 1e3 / HBM_PEAK_GBS
+            # the kernel's rate as a fraction of the stream's rate
+            r["frac_of_same_shape_stream"] = (nbytes / r["us"]) / (ceil_bytes / cm)
+            e[cond] = r
+        # headline figures: steady
+        for key in ("us", "p90_us", "gbps", "frac", "rows_per_s", "launches_timed"):
+            e[key] = e["steady"][key]
+        e["condition"] = "steady"
+        e["copy_ceiling_frac"] = e["gbps"] / copy_gbs["steady"]
+        e["traffic"] = measured_traffic(traffic_name)
+        e["traffic_source"] = TRAFFIC_SOURCE
+        return e
+
+    k_comp = kernel_entry(t_comp, c_comp, comp_bytes, cs_bytes, c3_rows, "compress_store")
+    k_gath = kernel_entry(t_gath, c_gath, gath_bytes, gs_bytes, n_ids, "dequant_gather")
     rows_step = c3_rows + n_ids
     value = rows_step / (ms_step / 1e3)
-    log(f"compress: {np.mean(comp_ms)*1e3:.1f} us  {comp_gbs:.0f} GB/s  "
-        f"gather: {np.mean(gath_ms)*1e3:.1f} us  {gath_gbs:.0f} GB/s  step {ms_step*1e3:.1f} us")
+    for name, k in (("compress", k_comp), ("gather", k_gath)):
+        log(f"{name}: steady {k['steady']['us']:.2f} us ({k['steady']['frac']:.3f}), cold "
+            f"{k['cold']['us']:.2f} us ({k['cold']['frac']:.3f}), cold_dirty "
+            f"{k['cold_dirty']['us']:.2f} us; same-shape stream "
+            f"{k['steady']['same_shape_stream_us']:.2f} / {k['cold']['same_shape_stream_us']:.2f}"
+            f" / {k['cold_dirty']['same_shape_stream_us']:.2f} us")
+    log(f"copy ceiling: steady {copy_gbs['steady']:.0f} GB/s, cold {copy_gbs['cold']:.0f} GB/s; "
+        f"step {ms_step * 1e3:.1f} us")
 
-    traffic = measured_traffic("dequant_gather")
     out = {
         "metric": "compressed KV rows/sec + achieved HBM GB/s (compress-store, dequant-gather)",
         "value": value,
@@ -518,64 +703,32 @@ def main() -> int:
             "workload": "prefill compress-store (ratio 2, 16 requests, 32768 tokens, fused "
                         "|kv|score| bf16 [32768,1024], page 128, V41_FP4) + sparse-prefill "
                         "dequant-gather (262144 ids from a 1048576-row V41 cache, page 64, "
-                        "random page table -> bf16 [262144,512]; 4 id lists used in turn)",
+                        "random page table -> bf16 [262144,512]; 4 disjoint id lists in turn)",
             "compress_rows": c3_rows, "gather_rows": n_ids,
             "seed_c3": int(c3["seed"]), "odd_lengths": c3_tails,
         },
         "hbm_gbps": (comp_bytes + gath_bytes) / (ms_step / 1e3) / 1e9,
-        "kernels": {
-            "compress_store": {"us": float(np.mean(comp_ms)) * 1e3, "p90_us": float(np.percentile(comp_ms, 90)) * 1e3,
-                               "launches_timed": 10 * runs,
-                               "bytes": comp_bytes, "gbps": comp_gbs, "frac": comp_gbs / HBM_PEAK_GBS,
-                               "rows_per_s": c3_rows / comp_s,
-                               "traffic": measured_traffic("compress_store")},
-            "dequant_gather": {"us": float(np.mean(gath_ms)) * 1e3, "p90_us": float(np.percentile(gath_ms, 90)) * 1e3,
-                               "launches_timed": 10 * runs,
-                               "bytes": gath_bytes, "gbps": gath_gbs, "frac": gath_gbs / HBM_PEAK_GBS,
-                               "rows_per_s": n_ids / gath_s},
-        },
-        "roofline": {"bound": "hbm", "achieved": gath_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gath_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "dequant_gather", "algorithmic_bytes": gath_bytes},
+        "kernels": {"compress_store": k_comp, "dequant_gather": k_gath},
+        "copy_ceiling": {"bytes_per_copy": 2 << 30, "steady_gbps": copy_gbs["steady"],
+                         "cold_gbps": copy_gbs["cold"],
+                         "steady_frac": copy_gbs["steady"] / HBM_PEAK_GBS,
+                         "cold_frac": copy_gbs["cold"] / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "achieved": k_gath["gbps"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": k_gath["frac"], "traffic": k_gath["traffic"],
+                     "traffic_source": TRAFFIC_SOURCE,
+                     "copy_ceiling_frac": k_gath["copy_ceiling_frac"],
+                     "condition": "steady", "kernel": "dequant_gather",
+                     "algorithmic_bytes": gath_bytes},
         "cpu_baseline": None,
     }
 
     if not args.no_next_rows:
-        out["next_rows"] = measure_next_rows(kvc, W, d, dev, stream)
+        out["next_rows"] = measure_next_rows(kvc, W, d, dev, torch.cuda.current_stream(), timer)
         out["next_rows"]["gather_reuse_c4_8_layers"] = measure_reuse(
-            kvc, g_cache, g_pt, g_idsets, g_outs, stream, layers=8)
+            kvc, g_cache, g_pt, g_idsets, g_outs, torch.cuda.current_stream(), layers=8)
 
-    # ---------------------------------------------------------------- oracle
     if not args.no_cpu_baseline:
-        import oracle
-        threads = oracle.num_threads()
-        # bounded sample: the first 4 requests of the compress batch and the
-        # first 65,536 gather ids, repeated until ~10 s of CPU work
-        n4 = int(lengths[:4].sum())
-        sub = dict(c3)
-        sub_off = c3["offsets"][:, :4].copy()
-        rows_sub = int((lengths[:4] // 2).sum())
-        m = 65536
-        ids_sub = c4["ids"][:m]
-        reps, spent, done_rows = 0, 0.0, 0
-        while spent < 10.0 and reps < 400:
-            cache_h = np.zeros((c3["num_pages"], 128 * fp4.row_bytes), np.uint8)
-            t = time.perf_counter()
-            oracle.compress(ratio=2, mode=oracle.PREFILL, kv=c3["kv"][:n4], fused=True,
-                            offsets=sub_off, start_pos=c3["start_pos"][:4],
-                            page_table=c3["page_table"][:4], state=c3["state"][:4].copy(),
-                            norm_w=c3["norm_w"], eps=c3["eps"], freqs=c3["freqs"], cache=cache_h,
-                            layout="V41_FP4", page_size=128, want_prequant=False)
-            oracle.dequant_gather(c4["cache"], "V41", 64, c4["page_table"], ids_sub)
-            spent += time.perf_counter() - t
-            done_rows += rows_sub + m
-            reps += 1
-        out["cpu_baseline"] = {"value": done_rows / spent, "unit": "rows/s", "cores": threads,
-                               "kind": "oracle",
-                               "sample": f"{reps} x (compress of the first 4 requests = "
-                                         f"{rows_sub} rows + gather of the first {m} ids), "
-                                         f"{spent:.1f} s"}
-        del sub
+        out["cpu_baseline"] = cpu_baseline(c3, c4, fp4.row_bytes)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -295,16 +295,17 @@ class KVBuf:
         return bool(hit.value)
 
 
-def kvc_compress_store(*, ratio: int, mode: int, kv: torch.Tensor, score: torch.Tensor | None,
+def _compress_args(*, ratio: int, mode: int, kv: torch.Tensor, score: torch.Tensor | None,
                        start_pos: torch.Tensor, cache: Cache, norm_w: torch.Tensor, eps: float,
                        freqs: torch.Tensor, latent_out: torch.Tensor, max_out_rows: int | None = None,
                        offsets: torch.Tensor | None = None, page_table: torch.Tensor | None = None,
                        out_loc: torch.Tensor | None = None, state: torch.Tensor | None = None,
                        prequant_out: torch.Tensor | None = None, status: torch.Tensor | None = None,
                        draft_len: int = 1, ring_slots: int = 1, dcp_world: int = 1,
-                       dcp_rank: int = 0, dcp_interleave: int = 1, tile_rows: int = 0,
-                       stream=None) -> None:
-    """The fused compressor.  ``kv``/``score`` are 2-D views whose row stride
+                       dcp_rank: int = 0, dcp_interleave: int = 1,
+                       tile_rows: int = 0) -> kvc_compress_args:
+    """The argument block of kvc_compress_store (every check done here).
+    The fused compressor.  ``kv``/``score`` are 2-D views whose row stride
     is passed through (a fused ``|kv|score|`` buffer ``proj [T, 1024]`` is
     ``kv=proj[:, :512], score=proj[:, 512:]``).  ``state`` is ``[S,
     ring_slots, 2, 512]`` bf16 (``[S, 2, 512]`` for one entry).  A page
@@ -367,4 +368,42 @@ def kvc_compress_store(*, ratio: int, mode: int, kv: torch.Tensor, score: torch.
     a.draft_len, a.ring_slots = draft_len, ring_slots
     a.dcp_world, a.dcp_rank, a.dcp_interleave = dcp_world, dcp_rank, dcp_interleave
     a.tile_rows = tile_rows
-    _check(lib().kvc_compress_store(C.byref(a), _stream(stream)))
+    return a
+
+
+def kvc_compress_store(*, stream=None, **kw) -> None:
+    """The fused compressor; keyword arguments as ``_compress_args``."""
+    _check(lib().kvc_compress_store(C.byref(_compress_args(**kw)), _stream(stream)))
+
+
+class Prepared:
+    """A call whose arguments were checked and packed once: calling it
+    launches on the given stream (default: the current one) with no Python
+    work beyond the foreign call.  It keeps the tensors it points to alive;
+    their contents may change between calls, their storage must not."""
+
+    __slots__ = ("_fn", "_args", "_keep")
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self, stream=None) -> None:
+        _check(self._fn(*self._args, _stream(stream)))
+
+
+def prepare_compress_store(**kw) -> Prepared:
+    """kvc_compress_store with its argument block built once."""
+    a = _compress_args(**kw)
+    return Prepared(lib().kvc_compress_store, (C.byref(a),), (a, kw))
+
+
+def prepare_dequant_gather(cache: Cache, page_table: torch.Tensor | None, ids: torch.Tensor,
+                           out: torch.Tensor, status: torch.Tensor | None = None) -> Prepared:
+    """kvc_dequant_gather with its arguments checked and packed once."""
+    _need(_rows_of(out, "out") >= ids.numel(), f"out: {out.shape[0]} rows for {ids.numel()} ids")
+    d = cache.desc()
+    n_pages = 0 if page_table is None else page_table.numel()
+    args = (C.byref(d), _opt(page_table, _dense, _I32_T, "page_table"), n_pages,
+            _dense(ids, _I32_T, "ids"), ids.numel(), _rows(out, _B16_T, "out"), out.stride(0),
+            _opt(status, _dense, _I32_T, "status"))
+    return Prepared(lib().kvc_dequant_gather, args, (d, cache, page_table, ids, out, status))

@@ -31,6 +31,7 @@ __all__ = [
     "paged_cache_shape", "random_cache_bytes", "compress_case", "decode_case",
     "store_case", "gather_case", "ragged_lengths", "verify_case", "rope_store_case",
     "dcp_ids_case", "per_rank_page_tables", "workload_c4_id_sets",
+    "workload_c4_disjoint_id_sets",
     "workload_c1", "workload_c2", "workload_c3", "workload_c4", "workload_c5",
 ]
 
@@ -433,6 +434,20 @@ def workload_c4_id_sets(count: int, n_ids: int = 262144, logical_pages: int = 16
         sets.append(rng.choice(logical_pages * page_size, size=n_ids,
                                replace=False).astype(np.int32))
     return sets
+
+
+def workload_c4_disjoint_id_sets(count: int, n_ids: int = 262144, logical_pages: int = 16384,
+                                 page_size: int = 64):
+    """``count`` id lists of the C4 gather that share no row: the workload's
+    own list first, then lists drawn without replacement from the rows it
+    leaves (so a timing loop's consecutive gathers read different rows)."""
+    first = workload_c4(n_ids, logical_pages, page_size)["ids"]
+    total = logical_pages * page_size
+    assert count * n_ids <= total
+    rest = np.setdiff1d(np.arange(total, dtype=np.int32), first)
+    rest = np.random.default_rng(BASE_SEED + 4 + 7000).permutation(rest)
+    return [first] + [rest[j * n_ids:(j + 1) * n_ids].astype(np.int32).copy()
+                      for j in range(count - 1)]
 
 
 def workload_c5(batch: int = 1024):
