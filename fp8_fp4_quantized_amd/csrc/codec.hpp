@@ -1,9 +1,17 @@
-// codec.hpp -- bit-exact number-format conversions for the KV row codecs.
+// codec.hpp -- number-format conversions for the KV row codecs.
 //
 // Formats: bfloat16; OCP fp8 e4m3fn (bias 7, max 448, 0x7F/0xFF NaN);
 // OCP fp4 e2m1 (values 0, .5, 1, 1.5, 2, 3, 4, 6); ue8m0 (a bare biased
-// exponent).  Encoders round to nearest, ties to even, and work on integer
-// bit fields so the result does not depend on any hardware rounding mode.
+// exponent).  Every encoder rounds to nearest, ties to even.  The ue8m0
+// exponent and the bf16 amax are integer work on bit fields; the fp8 and
+// e2m1 codes and the bf16 packing come from gfx950's conversion instructions
+// (v_cvt_scalef32_pk_fp8_f32, v_cvt_scalef32_pk_fp4_f32, v_cvt_pk_bf16_f32),
+// which round to nearest even whatever the shader's float mode.  Each
+// hardware path was checked on the device against the format's definition
+// over every input the quantizers can meet: fp8 codes for every finite bf16
+// under every ue8m0 exponent in range, e2m1 codes for every finite bf16
+// under every positive e4m3 scale, and the dequant conversions for every
+// code under every scale byte.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -67,8 +75,9 @@ __device__ __forceinline__ uint32_t fp8x4_scaled(float a, float b, float c, floa
 
 // Correctly rounded fp32 quotient x / s from rs, an fp32 within an ulp of
 // 1 / s (the nearest fp32, or v_rcp_f32): q0 = x * rs, the residual
-// x - q0 * s (exact in one fma) and one correction step.  Used for the FP4 group scale amax / 6 (equal to the fp32 division
-// for every finite bf16 amax >= 0) and for the element quotients x / s of the
+// x - q0 * s (exact in one fma) and one correction step.  Used for the FP4
+// group scale amax / 6 (equal to the fp32 division for every finite bf16
+// amax >= 0) and for the element quotients x / s of the
 // e2m1 codes (equal for every finite bf16 x with |x| <= 8 s under every
 // positive finite e4m3 s; the quantizer's quotients are at most about 6.4).
 // Both were checked exhaustively on the device against the division.  The

@@ -226,6 +226,66 @@ def test_gather_reuse_head(K):
     assert kb.kvc_dequant_gather_reuse(cache, pt, ids, out) is False
 
 
+def test_gather_reuse_head_follows_the_oracle_model(K):
+    """A random sequence of layers over three sources (V41, V41_FP4, V4
+    caches), three id lists and two row counts, with plain gets, output
+    reallocations and new forwards: every hit flag of kvc_dequant_gather_reuse
+    equals the oracle model's (sglang PR #45909, summary), and after every
+    operation the output buffer holds exactly the model's rows (the oracle's
+    gather of the head's ids)."""
+    from oracle.reuse_head import SparsePrefillKVBuffer
+    _say("gather reuse vs the oracle model")
+    rng = np.random.default_rng(9300)
+    geo = {"V41": (528, 512, 16), "V41_FP4": (288, 256, 32), "V4": (584, 576, 8)}
+    srcs = []
+    for s, layout in enumerate(geo):
+        c = W.gather_case(9301 + s, 24, 32, 64, *geo[layout],
+                          scale_lo=None if layout == "V41_FP4" else 114)
+        srcs.append((c, layout, K.Cache(dev(c["cache"]), layout, 32), dev(c["page_table"])))
+    id_lists = [rng.choice(24 * 32, size=700, replace=False).astype(np.int32) for _ in range(3)]
+    counts = (700, 513)
+    ids_dev = {(j, n): dev(id_lists[j][:n]) for j in range(3) for n in counts}
+
+    def fresh(s, j, n):
+        c, layout = srcs[s][0], srcs[s][1]
+        rows, st = oracle.dequant_gather(c["cache"], layout, 32, c["page_table"], id_lists[j][:n])
+        assert st == 0
+        return rows
+
+    model = SparsePrefillKVBuffer(fresh)
+    kb = K.KVBuf()
+    out = torch.zeros((700, 512), dtype=torch.int16, device="cuda")
+    hits = 0
+    for step in range(120):
+        op = rng.choice(["reuse", "reuse", "same", "same", "get", "realloc", "forward"])
+        if op == "same" and model.head is not None:
+            s, j, n = model.head
+            op = "reuse"
+        else:
+            s, j, n = int(rng.integers(0, 3)), int(rng.integers(0, 3)), counts[rng.integers(0, 2)]
+        c, layout, cache, pt = srcs[s]
+        if op == "reuse":
+            rows, want = model.get_with_head(s, j, n)
+            got = kb.kvc_dequant_gather_reuse(cache, pt, ids_dev[(j, n)], out[:n])
+            assert got == want, step
+            hits += got
+        elif op == "get":
+            rows = model.get(s, j, n)
+            K.kvc_dequant_gather(cache, pt, ids_dev[(j, n)], out[:n])
+            kb.forget()
+        elif op == "realloc":
+            model.reallocate()
+            out = torch.zeros((700, 512), dtype=torch.int16, device="cuda")
+            continue
+        else:
+            model.begin_forward()
+            kb.begin_forward()
+            continue
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out[:n], np.uint16), rows), step
+    assert hits >= 10
+
+
 # ===================================================================== compress
 _run_compress = run_compress
 _check_compress = check_compress
