@@ -648,6 +648,12 @@ def main() -> int:
     t_copy = {"steady": timer.steady(cp_calls), "cold": timer.flushed(cp_calls, dirty=False)}
     timer.launches = saved
     copy_gbs = {c: (2 << 30) / float(np.median(v)) / 1e3 for c, v in t_copy.items()}
+    # what a lone launch costs beyond its kernel under the cold flushes: a
+    # one-element kernel timed the same way
+    tiny = torch.zeros(1, dtype=torch.int32, device=dev)
+    call_overhead = {"cold": float(np.median(timer.flushed([lambda: tiny.add_(1)], dirty=False))),
+                     "cold_dirty": float(np.median(timer.flushed([lambda: tiny.add_(1)],
+                                                                 dirty=True)))}
     del cs_src, cs_out, cs_calls, gs_src, gs_out, gs_calls, cp, cp_calls
 
     def kernel_entry(t, c, nbytes, ceil_bytes, rows, traffic_name):
@@ -709,6 +715,7 @@ def main() -> int:
         },
         "hbm_gbps": (comp_bytes + gath_bytes) / (ms_step / 1e3) / 1e9,
         "kernels": {"compress_store": k_comp, "dequant_gather": k_gath},
+        "lone_call_overhead_us": call_overhead,
         "copy_ceiling": {"bytes_per_copy": 2 << 30, "steady_gbps": copy_gbs["steady"],
                          "cold_gbps": copy_gbs["cold"],
                          "steady_frac": copy_gbs["steady"] / HBM_PEAK_GBS,
