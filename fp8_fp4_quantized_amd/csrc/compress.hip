@@ -338,15 +338,7 @@ __device__ void build_tables(const CompressParams& p, int32_t* item_start, int32
       if (!in_buf && blockIdx.x == 0 && p.status != nullptr) atomicOr(p.status, kStTokenRange);
       sw = slot_work<RATIO>(in_buf ? n : 0, p.start_pos[b], p.tile_log2);
     }
-    int32_t si = sw.items, sr = sw.rows;
-#pragma unroll
-    for (int d = 1; d < kLanes; d <<= 1) {
-      const int32_t ti = __shfl_up(si, d), tr = __shfl_up(sr, d);
-      if (lane >= d) {
-        si += ti;
-        sr += tr;
-      }
-    }
+    const int32_t si = wave_incl_scan_i32(sw.items), sr = wave_incl_scan_i32(sw.rows);
     if (lane == kLanes - 1) {
       tot_i[wid] = si;
       tot_r[wid] = sr;
@@ -466,15 +458,8 @@ __global__ __launch_bounds__(kBlock) void compress_prefill_small_kernel(Compress
     if (blockIdx.x == 0 && p.status != nullptr) atomicOr(p.status, kStTokenRange);
   }
   const SlotWork sw = lane < S ? slot_work<RATIO>(n, P, p.tile_log2) : SlotWork{0, 0, 0, false};
-  int32_t inc_i = sw.items, inc_r = sw.rows;
-#pragma unroll
-  for (int d = 1; d < kLanes; d <<= 1) {
-    const int32_t ti = __shfl_up(inc_i, d), tr = __shfl_up(inc_r, d);
-    if (lane >= d) {
-      inc_i += ti;
-      inc_r += tr;
-    }
-  }
+  // inclusive sums over the slots (DPP scan: the first item's loads wait on it)
+  const int32_t inc_i = wave_incl_scan_i32(sw.items), inc_r = wave_incl_scan_i32(sw.rows);
   const float w[8] = {bf16_lo(wr.x), bf16_hi(wr.x), bf16_lo(wr.y), bf16_hi(wr.y),
                       bf16_lo(wr.z), bf16_hi(wr.z), bf16_lo(wr.w), bf16_hi(wr.w)};
   const int32_t total = __builtin_amdgcn_readlane(inc_i, kLanes - 1);
@@ -531,15 +516,7 @@ __global__ __launch_bounds__(kBlock) void compress_prefill_multi_kernel(Compress
     tot_r += sw.rows;
   }
   // inclusive scan of the lanes' totals, then each slot's inclusive sums
-  int32_t inc_i = tot_i, inc_r = tot_r;
-#pragma unroll
-  for (int d = 1; d < kLanes; d <<= 1) {
-    const int32_t ti = __shfl_up(inc_i, d), tr = __shfl_up(inc_r, d);
-    if (lane >= d) {
-      inc_i += ti;
-      inc_r += tr;
-    }
-  }
+  const int32_t inc_i = wave_incl_scan_i32(tot_i), inc_r = wave_incl_scan_i32(tot_r);
   int32_t ci[SPL], cr[SPL];
   {
     int32_t ri = inc_i - tot_i, rr = inc_r - tot_r;

@@ -52,6 +52,24 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Inclusive prefix sum over the 64 lanes: within each 16-lane row by DPP
+// row shifts of 1, 2, 4 and 8 (lanes past a row's start read 0), then the
+// row totals carried across rows by the row_bcast:15 / row_bcast:31
+// broadcasts -- six VALU steps, no LDS round trip.
+template <int Ctrl>
+__device__ __forceinline__ int32_t dpp_shr_or_zero(int32_t v) {
+  return __builtin_amdgcn_update_dpp(0, v, Ctrl, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int32_t wave_incl_scan_i32(int32_t v) {
+  v += dpp_shr_or_zero<0x111>(v);               // row_shr:1
+  v += dpp_shr_or_zero<0x112>(v);               // row_shr:2
+  v += dpp_shr_or_zero<0x114>(v);               // row_shr:4
+  v += dpp_shr_or_zero<0x118>(v);               // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);   // rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);   // rows 2, 3
+  return v;
+}
+
 // Pack one byte from each of four lanes spaced D apart into a dword on the
 // last of them: lane l receives byte(v[l-3D]) | byte(v[l-2D]) << 8 |
 // byte(v[l-D]) << 16 | byte(v[l]) << 24.  The lanes read must lie in l's
