@@ -134,14 +134,16 @@ def test_strided_buffers(K):
     assert np.array_equal(g[:, :512], want) and np.all(g[:, 512:] == 5)
 
 
-@pytest.mark.parametrize("n", [1, 31, 33, 97])
-@pytest.mark.parametrize("layout", ["V4", "V41_FP4"])
+@pytest.mark.parametrize("n", [1, 15, 17, 31, 33, 97, 131085])
+@pytest.mark.parametrize("layout", ["V4", "V41", "V41_FP4"])
 def test_gather_ragged_counts(K, n, layout):
-    """id counts that are not a multiple of the 32-id batch or the 8-row
-    unroll, through a page table."""
+    """id counts that are not a multiple of the id batch or of the rows a
+    wave expands per trip (16; 8 for V4), through a page table.  Below 2^17
+    ids the batch is 8; 131,085 ids take 32-id batches and end on a batch of
+    13."""
     _say("gather ragged", n, layout)
     db, sb, rb, _ = oracle.layout_bytes(layout)
-    c = W.gather_case(430 + n, 8, 16, n, rb, db, sb,
+    c = W.gather_case(430 + n, 8 if n <= 128 else n // 16 + 8, 16, n, rb, db, sb,
                       scale_lo=None if layout == "V41_FP4" else 110, scale_hi=140)
     want, st = oracle.dequant_gather(c["cache"], layout, 16, c["page_table"], c["ids"])
     out = torch.full((n + 1, 512), 9, dtype=torch.int16, device="cuda")
