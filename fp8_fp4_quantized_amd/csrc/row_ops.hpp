@@ -50,20 +50,22 @@ __device__ __forceinline__ void st_u4_stream(void* base, uint32_t byte_off, uint
 }
 
 // Loads through a buffer descriptor made from a base that is the same on
-// every lane, at a 32-bit byte offset below 2^31.  The _stream forms are
-// non-temporal at device scope (nt | sc1), for bytes read once and not
-// wanted in the L2; the _dev form is a cached load at device scope (sc1),
-// for bytes whose cache line other waves of the launch also read.
-__device__ __forceinline__ uint4 ld_u4_stream(const void* base, uint32_t byte_off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(raw_rsrc(base), (int)byte_off, 0, kCpolNtSc1);
+// every lane, at a 32-bit byte offset below 2^31, at device scope (sc1):
+// cached (CPOL = kCpolSc1), or non-temporal (kCpolNtSc1) for bytes read once
+// and not wanted in the L2.
+template <int CPOL>
+__device__ __forceinline__ uint4 ld_u4_buf(const void* base, uint32_t byte_off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(raw_rsrc(base), (int)byte_off, 0, CPOL);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ uint2 ld_u2_stream(const void* base, uint32_t byte_off) {
-  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(raw_rsrc(base), (int)byte_off, 0, kCpolNtSc1);
+template <int CPOL>
+__device__ __forceinline__ uint2 ld_u2_buf(const void* base, uint32_t byte_off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(raw_rsrc(base), (int)byte_off, 0, CPOL);
   return make_uint2(v.x, v.y);
 }
-__device__ __forceinline__ uint32_t ld_u32_stream(const void* base, uint32_t byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(raw_rsrc(base), (int)byte_off, 0, kCpolNtSc1);
+template <int CPOL>
+__device__ __forceinline__ uint32_t ld_u32_buf(const void* base, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(raw_rsrc(base), (int)byte_off, 0, CPOL);
 }
 __device__ __forceinline__ uint32_t ld_u8_dev(const void* base, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b8(raw_rsrc(base), (int)byte_off, 0, kCpolSc1);

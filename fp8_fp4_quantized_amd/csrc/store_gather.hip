@@ -199,57 +199,51 @@ __global__ __launch_bounds__(kBlock) void dcp_filter_kernel(DcpFilterParams p) {
 }
 
 // ------------------------------------------------------------------ gather
-// rows handled together by one wave per loop trip: 16 (0.5% faster than 8
-// on a 262,144-id V41 gather; 32 needs more registers than eight waves per
-// SIMD allow and ran 48% slower), 8 for V4, whose 16-byte lane shares of 16
-// rows would not fit those registers; and the most ids one wave resolves
-// per batch
-template <int L> constexpr int gather_unroll() { return L == kV4 ? 8 : 16; }
+// The most ids one wave resolves per batch, and the fewest.
 constexpr int kGatherBatch = 32;
 constexpr int kGatherMinBatch = 8;
+// A large gather (from 2^17 ids: its codes alone fill the chip's 32 MiB of
+// L2) streams its codes past the L2 and expands 16 rows per loop trip (0.5%
+// faster than 8 on 262,144 V41 ids; 32 needs more registers than eight waves
+// per SIMD allow and ran 48% slower); V4 keeps 8, whose 16-byte lane shares
+// of 16 rows would not fit those registers.  A smaller gather caches its
+// codes and takes 8 rows per trip (its batches hold at most 8 to 16 ids;
+// 16-row trips measured 10% slower on 18,642 ids).
+constexpr int64_t kLargeGatherIds = int64_t(1) << 17;
+template <int L, bool LARGE> constexpr int gather_unroll() { return LARGE && L != kV4 ? 16 : 8; }
 
 template <int L> struct LaneCodes;          // this lane's share of a row
 template <> struct LaneCodes<kV41> { uint2 codes; uint32_t scale; };
 template <> struct LaneCodes<kV41Fp4> { uint32_t codes; uint32_t scale; };
 template <> struct LaneCodes<kV4> { uint4 raw; uint32_t scale; };
 
-template <int L>
-__device__ __forceinline__ LaneCodes<L> load_lane(const PagedKV<L>& kv, int64_t slot, int lane);
-
-// Loads from the row's own base (the slot is the same on every lane).  The
-// codes are read once, so they are loaded non-temporally: the L2 then keeps
-// what the launch reads more than once, the ids, the page-table entries and
-// the scale lines (0.75 us faster on a 262,144-id gather than cached loads).
-// A row's scale part shares its cache line with the scale parts of the
-// page's other rows, so it is a cached load (non-temporal: 6% slower).
-template <>
-__device__ __forceinline__ LaneCodes<kV41> load_lane<kV41>(const PagedKV<kV41>& kv, int64_t slot,
-                                                           int lane) {
-  LaneCodes<kV41> r;
-  r.codes = ld_u2_stream(kv.data(slot), 8u * lane);
-  r.scale = ld_u8_dev(kv.scale(slot), (uint32_t)lane >> 2);
-  return r;
-}
-template <>
-__device__ __forceinline__ LaneCodes<kV41Fp4> load_lane<kV41Fp4>(const PagedKV<kV41Fp4>& kv,
-                                                                 int64_t slot, int lane) {
-  LaneCodes<kV41Fp4> r;
-  r.codes = ld_u32_stream(kv.data(slot), 4u * lane);
-  r.scale = ld_u8_dev(kv.scale(slot), (uint32_t)lane >> 1);
-  return r;
-}
-template <>
-__device__ __forceinline__ LaneCodes<kV4> load_lane<kV4>(const PagedKV<kV4>& kv, int64_t slot,
-                                                         int lane) {
-  LaneCodes<kV4> r;
-  const uint8_t* d = kv.data(slot);
-  if (lane < kRopeLane0) {
-    const uint2 c = ld_u2_stream(d, 8u * lane);
-    r.raw = make_uint4(c.x, c.y, 0u, 0u);
-    r.scale = ld_u8_dev(kv.scale(slot), (uint32_t)lane >> 3);
+// Loads from the row's own base (the slot is the same on every lane).  A
+// row's scale part shares its cache line with the scale parts of the page's
+// other rows, so it is always a cached load (non-temporal: 6% slower on a
+// 262,144-id gather).  The codes take CPOL: a large gather reads each row
+// once and loads them non-temporally, so that the L2 keeps what the launch
+// reads more than once -- the ids, the page-table entries and the scale
+// lines (0.75 us faster on 262,144 ids than cached loads); a small gather
+// caches them, since the next call may read the same rows again.
+template <int L, int CPOL>
+__device__ __forceinline__ LaneCodes<L> load_lane(const PagedKV<L>& kv, int64_t slot, int lane) {
+  LaneCodes<L> r;
+  if constexpr (L == kV41) {
+    r.codes = ld_u2_buf<CPOL>(kv.data(slot), 8u * lane);
+    r.scale = ld_u8_dev(kv.scale(slot), (uint32_t)lane >> 2);
+  } else if constexpr (L == kV41Fp4) {
+    r.codes = ld_u32_buf<CPOL>(kv.data(slot), 4u * lane);
+    r.scale = ld_u8_dev(kv.scale(slot), (uint32_t)lane >> 1);
   } else {
-    r.raw = ld_u4_stream(d, kNope + 16u * (lane - kRopeLane0));
-    r.scale = 0;
+    const uint8_t* d = kv.data(slot);
+    if (lane < kRopeLane0) {
+      const uint2 c = ld_u2_buf<CPOL>(d, 8u * lane);
+      r.raw = make_uint4(c.x, c.y, 0u, 0u);
+      r.scale = ld_u8_dev(kv.scale(slot), (uint32_t)lane >> 3);
+    } else {
+      r.raw = ld_u4_buf<CPOL>(d, kNope + 16u * (lane - kRopeLane0));
+      r.scale = 0;
+    }
   }
   return r;
 }
@@ -276,14 +270,14 @@ __device__ __forceinline__ uint4 decode_lane<kV4>(const LaneCodes<kV4>& c, int l
 // a time, their slots broadcast with v_readlane, all their loads issued before
 // any store.  32-id batches give 8192 waves for 262,144 ids, one resident
 // round of the chip at eight waves per SIMD (measured faster than 16, 48 or
-// 64); a smaller
-// gather takes smaller batches, so that its rows spread over more waves.
-// Eight waves per SIMD asked of the compiler: it then keeps the kernel to 78
-// scalar registers (93 otherwise), and the launch's 8192 waves go through
-// 0.9% faster.
-template <int L>
+// 64); a smaller gather takes smaller batches, so that its rows spread over
+// more waves.  Eight waves per SIMD asked of the compiler: it then keeps the
+// kernel to 78 scalar registers (93 otherwise), and the launch's 8192 waves
+// go through 0.9% faster.
+template <int L, bool LARGE>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void dequant_gather_kernel(GatherParams p) {
+  constexpr int CPOL = LARGE ? kCpolNtSc1 : kCpolSc1;
   const PagedKV<L> kv = paged<L>(p.cache);
   const int lane = lane_id();
   const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
@@ -322,14 +316,14 @@ void dequant_gather_kernel(GatherParams p) {
 
     // ---- expand the batch's rows
     const int cnt = (int)(p.n - b0 < batch ? p.n - b0 : batch);
-    constexpr int U = gather_unroll<L>();
+    constexpr int U = gather_unroll<L, LARGE>();
     for (int j = 0; j < cnt; j += U) {
       int32_t s[U];
       LaneCodes<L> c[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         s[u] = j + u < cnt ? __builtin_amdgcn_readlane(slot, j + u) : -1;
-        if (s[u] >= 0) c[u] = load_lane<L>(kv, s[u], lane);
+        if (s[u] >= 0) c[u] = load_lane<L, CPOL>(kv, s[u], lane);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -386,10 +380,17 @@ hipError_t launch_dequant_gather(const GatherParams& p_in, hipStream_t stream) {
   p.batch = kGatherBatch;
   while (p.batch > kGatherMinBatch && p.n < (int64_t)p.batch * 4096) p.batch >>= 1;
   const int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * p.batch, 8192);
+  const bool large = p.n >= kLargeGatherIds;
   switch (p.cache.layout) {
-    case kV41: return launch(dequant_gather_kernel<kV41>, blocks, p, stream);
-    case kV41Fp4: return launch(dequant_gather_kernel<kV41Fp4>, blocks, p, stream);
-    default: return launch(dequant_gather_kernel<kV4>, blocks, p, stream);
+    case kV41:
+      return large ? launch(dequant_gather_kernel<kV41, true>, blocks, p, stream)
+                   : launch(dequant_gather_kernel<kV41, false>, blocks, p, stream);
+    case kV41Fp4:
+      return large ? launch(dequant_gather_kernel<kV41Fp4, true>, blocks, p, stream)
+                   : launch(dequant_gather_kernel<kV41Fp4, false>, blocks, p, stream);
+    default:
+      return large ? launch(dequant_gather_kernel<kV4, true>, blocks, p, stream)
+                   : launch(dequant_gather_kernel<kV4, false>, blocks, p, stream);
   }
 }
 
