@@ -10,8 +10,8 @@ Inputs are seeded synthetic data, resident in HBM before timing starts.
 
 Prints one JSON line.  ``value`` is compressed KV rows per second over the
 timed steps (rows compressed + rows gathered).  Each headline kernel is also
-timed launch by launch (median and p90 over --launches calls) under three
-cache conditions:
+timed under three cache conditions, median and p90 (steady: 10 samples of 50
+launches; the cold ones: --launches lone calls):
   steady      back to back, every call on other buffers than the calls
               before it (no reuse of what they left in the 256 MB Infinity
               Cache), as in a pipeline that keeps the device busy;
@@ -74,9 +74,11 @@ TRAFFIC_SOURCE = ("profiles/traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE pe
 class Timer:
     """Device time per launch of a kernel under three cache conditions, from
     HIP events on the launch stream (calls[k % len] is launch k):
-      steady      a HIP graph of 10 back-to-back launches, replayed after an
+      steady      a HIP graph of 50 back-to-back launches, replayed after an
                   untimed lead-in replay; one sample per replay (its mean per
-                  launch), so no host launch cost falls inside an interval;
+                  launch), 10 replays.  No host launch cost falls inside an
+                  interval, and the device's own gap before a replay's first
+                  kernel (about 10 us) is spread over 50 launches;
       cold        lone launches, each after a 512 MB scratch write and a
                   512 MB scratch read (neither timed), each bracketed by
                   events: the caches hold none of the call's data and no
@@ -86,7 +88,8 @@ class Timer:
       cold_dirty  the same after the scratch write alone: the interval also
                   carries the write-back of the scratch's dirty lines."""
 
-    PER_GRAPH = 10
+    PER_GRAPH = 50
+    REPLAYS = 10
 
     def __init__(self, dev, launches: int):
         import torch
@@ -100,7 +103,7 @@ class Timer:
     def read_flush(self):
         self.torch.amax(self.scratch.view(self.torch.int64))
 
-    def steady(self, calls):
+    def steady(self, calls, replays: int = REPLAYS):
         torch = self.torch
         n = self.PER_GRAPH
         body = lambda: [calls[k % len(calls)]() for k in range(n)]
@@ -117,7 +120,7 @@ class Timer:
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         samples = []
-        for _ in range(max(1, self.launches // n)):
+        for _ in range(replays):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             g.replay()                       # untimed lead-in: the device is busy
             a.record(stream)
@@ -387,8 +390,8 @@ def measure_sweep(kvc, W, d, dev, stream):
     """Throughput against size: the prefill compress at 1, 2, 4 and 8 times
     the 32,768-token workload (16 requests per 32,768 ragged tokens, fused
     |kv|score| buffer, page 128, V41_FP4), and the gather from the 1,048,576-row
-    V41 cache at 65,536 to 1,048,576 distinct ids (four id lists and three
-    outputs in turn).  Each size is timed as graph replays of back-to-back
+    V41 cache at 65,536 to 1,048,576 distinct ids (four id lists, disjoint
+    where the cache's rows allow, and three outputs in turn).  Each size is timed as graph replays of back-to-back
     calls, like the next rows, with its inputs and outputs in turn."""
     import numpy as np
     import torch
@@ -444,9 +447,12 @@ def measure_sweep(kvc, W, d, dev, stream):
         torch.cuda.empty_cache()
     c4 = W.workload_c4()
     cache, pt = kvc.Cache(d(c4["cache"]), "V41", 64), d(c4["page_table"])
+    rows = 1048576
     for n in (65536, 262144, 524288, 1048576):
-        sets = [d(np.random.default_rng(W.BASE_SEED + 200 + j).choice(
-            1048576, size=n, replace=False).astype(np.int32)) for j in range(4)]
+        # four lists cut in turn from one random order of the cache's rows:
+        # disjoint up to 262,144 ids, each row in at most two lists at 524,288
+        order = np.random.default_rng(W.BASE_SEED + 200 + n).permutation(rows).astype(np.int32)
+        sets = [d(np.take(order, np.arange(j * n, (j + 1) * n) % rows)) for j in range(4)]
         outs = [torch.empty((n, 512), dtype=torch.int16, device=dev) for _ in range(3)]
         turn = [0]
 
@@ -518,7 +524,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--launches", type=int, default=100,
-                    help="timed launches per kernel and cache condition (median, p90)")
+                    help="timed lone launches per kernel in each cold condition (median, p90)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the verify / RoPE-store / DCP-filter / graph-replay / reuse measurements")
@@ -645,7 +651,8 @@ def main() -> int:
            torch.empty(1 << 30, dtype=torch.uint8, device=dev)) for _ in range(2)]
     cp_calls = [lambda s=s_, t=t_: t.copy_(s) for s_, t_ in cp]
     saved, timer.launches = timer.launches, 10
-    t_copy = {"steady": timer.steady(cp_calls), "cold": timer.flushed(cp_calls, dirty=False)}
+    t_copy = {"steady": timer.steady(cp_calls, replays=2),
+              "cold": timer.flushed(cp_calls, dirty=False)}
     timer.launches = saved
     copy_gbs = {c: (2 << 30) / float(np.median(v)) / 1e3 for c, v in t_copy.items()}
     # what a lone launch costs beyond its kernel under the cold flushes: a
@@ -658,8 +665,9 @@ def main() -> int:
 
     def kernel_entry(t, c, nbytes, ceil_bytes, rows, traffic_name):
         e = {"bytes": nbytes, "rows": rows,
-             "timing": "steady: HIP events around HIP-graph replays of 10 back-to-back launches, "
-                       "one sample per replay; cold, cold_dirty: lone launches after the flush, "
+             "timing": "steady: HIP events around 10 HIP-graph replays of 50 back-to-back "
+                       "launches, one sample per replay; cold, cold_dirty: lone launches after "
+                       "the flush, "
                        "each bracketed by events (dispatch and completion included)"}
         for cond in ("steady", "cold", "cold_dirty"):
             r = summarize(t[cond], nbytes, rows, "rows_per_s",
