@@ -134,13 +134,15 @@ def test_strided_buffers(K):
     assert np.array_equal(g[:, :512], want) and np.all(g[:, 512:] == 5)
 
 
-@pytest.mark.parametrize("n", [1, 15, 17, 31, 33, 97, 131085])
+@pytest.mark.parametrize("n", [1, 15, 17, 31, 33, 97, 65537, 131071, 131072, 131085])
 @pytest.mark.parametrize("layout", ["V4", "V41", "V41_FP4"])
 def test_gather_ragged_counts(K, n, layout):
     """id counts that are not a multiple of the id batch or of the rows a
-    wave expands per trip (16; 8 for V4), through a page table.  Below 2^17
-    ids the batch is 8; 131,085 ids take 32-id batches and end on a batch of
-    13."""
+    wave expands per trip, through a page table.  Up to 65,535 ids the batch
+    is 8 and a trip 8 rows; 65,537 and 131,071 ids take 16-id batches and
+    8-row trips, the last batch short; from 131,072 ids (the large-gather
+    form: streamed codes, 16-row trips except V4) 32-id batches, and
+    131,085 ids end on a batch of 13."""
     _say("gather ragged", n, layout)
     db, sb, rb, _ = oracle.layout_bytes(layout)
     c = W.gather_case(430 + n, 8 if n <= 128 else n // 16 + 8, 16, n, rb, db, sb,
