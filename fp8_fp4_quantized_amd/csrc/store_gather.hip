@@ -211,6 +211,12 @@ constexpr int kGatherMinBatch = 8;
 // 16-row trips measured 10% slower on 18,642 ids).
 constexpr int64_t kLargeGatherIds = int64_t(1) << 17;
 template <int L, bool LARGE> constexpr int gather_unroll() { return LARGE && L != kV4 ? 16 : 8; }
+// workgroup of a large gather: 8 waves (0.6% faster than 4 on 262,144 V41
+// ids; 2 and 16 slower); a smaller gather keeps 4
+template <bool LARGE> constexpr int gather_block() { return LARGE ? 512 : kBlock; }
+// most waves of a gather's grid (2^20 ids at 32 per batch); rows past them
+// take further turns
+constexpr int64_t kGatherMaxWaves = 32768;
 
 template <int L> struct LaneCodes;          // this lane's share of a row
 template <> struct LaneCodes<kV41> { uint2 codes; uint32_t scale; };
@@ -275,13 +281,14 @@ __device__ __forceinline__ uint4 decode_lane<kV4>(const LaneCodes<kV4>& c, int l
 // kernel to 78 scalar registers (93 otherwise), and the launch's 8192 waves
 // go through 0.9% faster.
 template <int L, bool LARGE>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8)))
+__global__ __launch_bounds__(gather_block<LARGE>()) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void dequant_gather_kernel(GatherParams p) {
   constexpr int CPOL = LARGE ? kCpolNtSc1 : kCpolSc1;
+  constexpr int kWaves = gather_block<LARGE>() / kLanes;
   const PagedKV<L> kv = paged<L>(p.cache);
   const int lane = lane_id();
-  const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const int64_t wave0 = uniform64((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6));
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
   const int32_t page_mask = (1 << p.cache.page_bits) - 1;
 
   const int32_t batch = p.batch;
@@ -379,18 +386,23 @@ hipError_t launch_dequant_gather(const GatherParams& p_in, hipStream_t stream) {
   GatherParams p = p_in;
   p.batch = kGatherBatch;
   while (p.batch > kGatherMinBatch && p.n < (int64_t)p.batch * 4096) p.batch >>= 1;
-  const int blocks = grid_for(p.n, (int64_t)kWavesPerBlock * p.batch, 8192);
   const bool large = p.n >= kLargeGatherIds;
+  const int block = large ? gather_block<true>() : gather_block<false>();
+  const int64_t waves_per_block = block / kLanes;
+  const int blocks = grid_for(p.n, waves_per_block * p.batch,
+                              (int)(kGatherMaxWaves / waves_per_block));
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(block), 0, stream, p);
+    return hipGetLastError();
+  };
   switch (p.cache.layout) {
     case kV41:
-      return large ? launch(dequant_gather_kernel<kV41, true>, blocks, p, stream)
-                   : launch(dequant_gather_kernel<kV41, false>, blocks, p, stream);
+      return large ? go(dequant_gather_kernel<kV41, true>) : go(dequant_gather_kernel<kV41, false>);
     case kV41Fp4:
-      return large ? launch(dequant_gather_kernel<kV41Fp4, true>, blocks, p, stream)
-                   : launch(dequant_gather_kernel<kV41Fp4, false>, blocks, p, stream);
+      return large ? go(dequant_gather_kernel<kV41Fp4, true>)
+                   : go(dequant_gather_kernel<kV41Fp4, false>);
     default:
-      return large ? launch(dequant_gather_kernel<kV4, true>, blocks, p, stream)
-                   : launch(dequant_gather_kernel<kV4, false>, blocks, p, stream);
+      return large ? go(dequant_gather_kernel<kV4, true>) : go(dequant_gather_kernel<kV4, false>);
   }
 }
 
