@@ -156,6 +156,31 @@ def test_gather_ragged_counts(K, n, layout):
     assert st == 0 and np.array_equal(g[:n], want) and np.all(g[n] == 9)
 
 
+@pytest.mark.parametrize("layout", ["V4", "V41", "V41_FP4"])
+def test_gather_large_strided_output(K, layout):
+    """a gather in the large form (140,001 ids, 32-id batches, streamed codes)
+    into a strided output (rows 640 elements apart), ids with -1 and ids past
+    the page table: rows and status equal the oracle's, the columns between
+    rows are untouched."""
+    _say("gather large strided", layout)
+    n = 140001
+    db, sb, rb, _ = oracle.layout_bytes(layout)
+    c = W.gather_case(470, n // 16 + 8, 16, n, rb, db, sb,
+                      scale_lo=None if layout == "V41_FP4" else 110, scale_hi=140)
+    ids = c["ids"].copy()
+    ids[::17] = -1
+    ids[5::1001] = (n // 16 + 8) * 16 + 3               # past the page table
+    want, st = oracle.dequant_gather(c["cache"], layout, 16, c["page_table"], ids)
+    out = torch.full((n, 640), 11, dtype=torch.int16, device="cuda")
+    s = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvc_dequant_gather(K.Cache(dev(c["cache"]), layout, 16), dev(c["page_table"]), dev(ids),
+                         out[:, :512], s)
+    torch.cuda.synchronize()
+    g = host(out, np.uint16)
+    assert np.array_equal(g[:, :512], want) and np.all(g[:, 512:] == 11)
+    assert int(s.item()) == st == K.STATUS_ID_RANGE
+
+
 def test_gather_grid_stride_sampled(K):
     """3,000,017 ids (random, 1% of them -1) from a 262,144-row V41 cache into
     a 3 GB output: past the gather grid's one-round capacity of 2^20 ids, so
