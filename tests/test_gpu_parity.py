@@ -390,6 +390,23 @@ def test_compress_many_requests_full(K, requests):
     _check_compress(r, "V41_FP4", 128, slots, lat)
 
 
+@pytest.mark.parametrize("requests", [16, 100, 300])
+def test_compress_prefill_many_passes(K, requests):
+    """twice the C3 batch (65,536 tokens, fused buffer, page 128, V41_FP4)
+    in 16, 100 or 300 ragged requests: about 16,380 work items on a grid of
+    4096 waves, so every wave takes four passes, the last one partial, through
+    the one-ballot, two-slots-per-lane and LDS-table kernels."""
+    _say("compress many passes", requests)
+    rng = np.random.default_rng(W.BASE_SEED + 50 + requests)
+    lengths = W.ragged_lengths(rng, 65536, requests)
+    case = W.compress_case(W.BASE_SEED + 51 + requests, lengths, ratio=2, page_size=128,
+                           fused=True, state_random=False)
+    r = _run_compress(K, case, "V41_FP4", 2, oracle.PREFILL)
+    lat, slots = _prefill_slots(case, 2)
+    assert r["n_rows"] == int((lengths // 2).sum()) == len(lat)
+    _check_compress(r, "V41_FP4", 128, slots, lat)
+
+
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_compress_ratio1_c2(K, layout):
     """fused ratio-1 compress (norm + rope) of the C2 rows, then a gather of
