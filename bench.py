@@ -200,9 +200,9 @@ def measure_next_rows(kvc, W, d, dev, stream, timer):
     """Throughput of the entry points beyond the two headline kernels, each on
     a workload of the path's own shapes, with its algorithmic HBM bytes.
     These are timed as graph replays of back-to-back calls on the same
-    buffers (warm, as a decode step's freshly written inputs would be); the
-    ratio-1 store and dequant rows of the 8-request workload are also timed
-    cold (the flush before each call, median and p90)."""
+    buffers (warm, as a decode step's freshly written inputs would be); each
+    is also timed cold: lone calls after the flush, median and p90, the
+    launch's dispatch and completion included."""
     import numpy as np
     import torch
 
@@ -237,8 +237,9 @@ def measure_next_rows(kvc, W, d, dev, stream, timer):
                  cache=kvc.Cache(torch.zeros((vc["num_pages"], 64 * fp4.row_bytes),
                                              dtype=torch.uint8, device=dev), "V41_FP4", 64),
                  draft_len=D, ring_slots=3, status=status)
-    secs = _time_events(lambda: kvc.kvc_compress_store(**vargs), stream, 50)
-    entry("verify_1024x4_v41fp4", secs, vbytes, rows, "rows_per_s")
+    v_call = lambda: kvc.kvc_compress_store(**vargs)
+    secs = _time_events(v_call, stream, 50)
+    entry("verify_1024x4_v41fp4", secs, vbytes, rows, "rows_per_s", v_call)
 
     # decode: 1024 slots x 1 token, ratio 2, explicit out_loc, V4 cache
     c5 = W.workload_c5()
@@ -254,8 +255,9 @@ def measure_next_rows(kvc, W, d, dev, stream, timer):
                  cache=kvc.Cache(torch.zeros((c5["num_pages"], 64 * v4.row_bytes),
                                              dtype=torch.uint8, device=dev), "V4", 64),
                  status=status)
-    secs = _time_events(lambda: kvc.kvc_compress_store(**dargs), stream, 50)
-    entry("decode_1024_v4", secs, dbytes, drows, "rows_per_s")
+    d_call = lambda: kvc.kvc_compress_store(**dargs)
+    secs = _time_events(d_call, stream, 50)
+    entry("decode_1024_v4", secs, dbytes, drows, "rows_per_s", d_call)
 
     # RoPE store: the ratio-1 store workload (8 requests, 512..4096 rows) with
     # a rotary position per row, into V41_FP4
@@ -285,9 +287,10 @@ def measure_next_rows(kvc, W, d, dev, stream, timer):
     dq_v41 = lambda: kvc.kvc_dequant_gather(vcache, None, rloc, dq_out, status)
     secs = _time_events(dq_v41, stream, 50)
     entry("dequant_c2_v41", secs, n2 * (v41c.row_bytes + 1024 + 4), n2, "rows_per_s", dq_v41)
-    secs = _time_events(lambda: kvc.kvc_store_rows_rope(rcache, rrows, pos2, fr2, rloc, status),
-                        stream, 50)
-    entry("rope_store_c2_v41fp4", secs, n2 * (1024 + fp4.row_bytes + 8), n2, "rows_per_s")
+    r_call = lambda: kvc.kvc_store_rows_rope(rcache, rrows, pos2, fr2, rloc, status)
+    secs = _time_events(r_call, stream, 50)
+    entry("rope_store_c2_v41fp4", secs, n2 * (1024 + fp4.row_bytes + 8), n2, "rows_per_s",
+          r_call)
 
     # DCP filter: 4096 tokens x 2048 global ids, 4 ranks, runs of 4, rank 1
     dc = W.dcp_ids_case(20261208, T=4096, k=2048, n_req=32, max_rows=65536, world=4,
@@ -297,10 +300,11 @@ def measure_next_rows(kvc, W, d, dev, stream, timer):
     f_valid = d(dc["valid"])
     f_out = torch.empty((T, k), dtype=torch.int32, device=dev)
     f_lens = torch.empty(T, dtype=torch.int32, device=dev)
-    secs = _time_events(lambda: kvc.kvc_dcp_filter_ids(
+    f_call = lambda: kvc.kvc_dcp_filter_ids(
         f_ids, f_t2r, f_bt, f_out, f_lens, page_size=64, num_pages=dc["num_pages"], world=4,
-        rank=1, interleave=4, valid=f_valid, status=status), stream, 50)
-    entry("dcp_filter_4096x2048_w4", secs, T * k * 8 + T * 12, T * k, "ids_per_s")
+        rank=1, interleave=4, valid=f_valid, status=status)
+    secs = _time_events(f_call, stream, 50)
+    entry("dcp_filter_4096x2048_w4", secs, T * k * 8 + T * 12, T * k, "ids_per_s", f_call)
 
     # graph replay vs eager launch of the small prefill compress (one 64-token
     # request, ratio 2, V41): host wall time per call, back to back
