@@ -71,13 +71,36 @@ TRAFFIC_SOURCE = ("profiles/traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE pe
                   "null once the kernel's sources differ from the counted build")
 
 
+WARM_UP_S = 0.025
+
+
+def warm_up_replays(g):
+    """Replay a freshly captured graph untimed for about WARM_UP_S of device
+    time (at least twice): the device idles while a graph is captured on the
+    host, and the replays just after that ran up to 10% slower (the first 10
+    ms or so).  Returns without waiting, so that the device is still busy
+    with these replays while the caller queues its timed ones: after a long
+    run of queued replays the host's next submissions can be slow, and a
+    timed interval that starts on an idle device would hold that wait."""
+    import torch
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    per = max(a.elapsed_time(b) / 1e3, 1e-6)
+    for _ in range(min(200, max(2, int(WARM_UP_S / per) + 1))):
+        g.replay()
+
+
 class Timer:
     """Device time per launch of a kernel under three cache conditions, from
     HIP events on the launch stream (calls[k % len] is launch k):
-      steady      a HIP graph of 50 back-to-back launches, replayed 10 times
-                  untimed, then 10 timed replays, each after an untimed
-                  lead-in replay; one sample per timed replay (its mean per
-                  launch).  No host launch cost falls inside an interval, and
+      steady      a HIP graph of 50 back-to-back launches, replayed untimed
+                  for about 25 ms, then 10 timed replays, each after an
+                  untimed lead-in replay; one sample per timed replay (its
+                  mean per launch).  No host launch cost falls inside an interval, and
                   the device's own gap before a replay's first kernel (about
                   10 us) is spread over 50 launches;
       cold        lone launches, each after a 512 MB scratch write and a
@@ -91,7 +114,6 @@ class Timer:
 
     PER_GRAPH = 50
     REPLAYS = 10
-    WARM_REPLAYS = 10
 
     def __init__(self, dev, launches: int):
         import torch
@@ -118,12 +140,7 @@ class Timer:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             body()
-        # untimed replays first: the device idles while the graph is captured
-        # on the host, and its first few replays after that run up to 10%
-        # slower
-        for _ in range(self.WARM_REPLAYS):
-            g.replay()
-        torch.cuda.synchronize()
+        warm_up_replays(g)
         stream = torch.cuda.current_stream()
         samples = []
         for _ in range(replays):
@@ -177,8 +194,9 @@ def summarize(samples_us, nbytes, units, unit_name, ceiling_us=None, per_sample=
 def _time_events(fn, stream, reps: int, warmup: int = 3):
     """mean device time in seconds of one fn() call.  The calls are captured
     back to back in a HIP graph so that host-side launch cost does not pace
-    them (small kernels run faster than Python can launch them); HIP events
-    on the replay stream bracket three replays of the graph."""
+    them (small kernels run faster than Python can launch them); after the
+    untimed warm-up replays, HIP events on the replay stream bracket three
+    replays of the graph."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -191,8 +209,7 @@ def _time_events(fn, stream, reps: int, warmup: int = 3):
     with torch.cuda.graph(g):
         for _ in range(reps):
             fn()
-    g.replay()
-    torch.cuda.synchronize()
+    warm_up_replays(g)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(3):
